@@ -1,0 +1,88 @@
+"""Split-count rules (oracle). TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Source: "Flash-Decoding: Split-KV Attention for Long-Context Decode" (kanthi.in)
+§6 "How many splits?" -- the wave-efficiency rule of the FlashAttention-2
+dispatcher -- and the same rule as explained in the FA3 comment quoted in the
+vatshank blog "Benchmarking split-KV against vanilla FA" (48 work items on 108
+SMs: 2 splits give efficiency 0.89, 3 splits 0.67).
+
+The rule, in words: launch W·S workgroups onto ``slots`` resident slots; a
+split count S fills a fraction W·S/slots of the machine, and the last wave of
+that launch is busy for frac(W·S/slots) of its length; S = 1 when W alone
+already fills 80 % of the slots; otherwise among the split counts up to
+min(max_splits, slots, n_blocks) that change the number of blocks per split,
+take the smallest one whose efficiency is at least 85 % of the best.
+
+``num_splits_fa2`` is that rule as the page states it (pinned by the page's
+printed table and by the FA3 comment's two efficiencies). ``num_splits_traffic``
+adds the overhead check at the end of §6 -- the fp32 workspace written and read
+back, relative to the KV bytes, must stay under a budget -- generalised to g
+query heads per KV head and (D + 2) floats per state; it is what the library's
+planner runs with the MI355X slot count. Its choices on MI355X are
+"parity unpinned": the pages give no MI355X numbers; measured split sweeps
+justify the defaults instead.
+"""
+from __future__ import annotations
+
+import math
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def wave_efficiency(work: int, splits: int, slots: int) -> float:
+    """Busy fraction of the last wave: w / ceil(w) with w = work·splits/slots."""
+    w = work * splits / slots
+    return w / math.ceil(w)
+
+
+def _eligible(s: int, n_blocks: int) -> bool:
+    """A split count is worth trying only if it changes the blocks per split."""
+    return s == 1 or cdiv(n_blocks, s) != cdiv(n_blocks, s - 1)
+
+
+def num_splits_fa2(work: int, slots: int, n_blocks: int, max_splits: int = 128) -> int:
+    """The §6 wave-efficiency rule."""
+    if work >= 0.8 * slots:
+        return 1
+    cap = min(max_splits, slots, n_blocks)
+    if cap <= 1:
+        return 1
+    cands = [s for s in range(1, cap + 1) if _eligible(s, n_blocks)]
+    eff = {s: wave_efficiency(work, s, slots) for s in cands}
+    best = max(eff.values())
+    return min(s for s in cands if eff[s] >= 0.85 * best)
+
+
+def workspace_ratio(splits: int, group: int, head_dim: int, kv_elt: int, max_len: int) -> float:
+    """Workspace bytes (written by the split kernel, read by the merge) per KV byte
+    for one (sequence, KV head): 2·S·g·(D+2)·4 / (2·L·D·elt). With g = 1, elt = 2
+    and the (D+2) taken as D this is the 2S/t of the §6 overhead check."""
+    if max_len <= 0:
+        return math.inf
+    return (2.0 * splits * group * (head_dim + 2) * 4.0) / (2.0 * max_len * head_dim * kv_elt)
+
+
+def num_splits_traffic(work: int, slots: int, n_blocks: int, max_splits: int, group: int,
+                       head_dim: int, kv_elt: int, max_len: int, budget: float) -> int:
+    """The §6 rule restricted to split counts whose workspace traffic stays within
+    ``budget`` of the KV bytes (S = 1 is always allowed). Parity unpinned."""
+    if work >= 0.8 * slots:
+        return 1
+    cap = min(max_splits, slots, n_blocks)
+    if cap <= 1:
+        return 1
+    cands = [s for s in range(1, cap + 1) if _eligible(s, n_blocks)
+             and (s == 1 or workspace_ratio(s, group, head_dim, kv_elt, max_len) <= budget)]
+    eff = {s: wave_efficiency(work, s, slots) for s in cands}
+    best = max(eff.values())
+    return min(s for s in cands if eff[s] >= 0.85 * best)
+
+
+def chunk_for(max_len: int, splits: int, align: int) -> int:
+    """Tokens per split: cdiv(max_len, S) (the §4 wrapper of the kanthi.in chapter)
+    rounded up to a multiple of ``align`` (KV page and/or tile; §7 aligns split
+    boundaries to KV pages)."""
+    c = max(1, cdiv(max(max_len, 1), splits))
+    return cdiv(c, align) * align

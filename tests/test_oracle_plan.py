@@ -1,0 +1,59 @@
+"""Pins of the oracle's split-count rules (kanthi.in §6; vatshank FA3 comment)."""
+import math
+
+from oracle import plan as P
+from tests.conftest import golden
+
+
+def test_page_split_table():
+    g = golden("split_table.json")
+    for row in g["rows"]:
+        work = row["batch"] * row["heads"]
+        assert work == row["work"]
+        n_blocks = math.ceil(row["context"] / g["block_n"])
+        s = P.num_splits_fa2(work, g["slots"], n_blocks, g["max_splits"])
+        assert s == row["splits"], row
+        assert work * s == row["ctas"]
+
+
+def test_fa3_comment_efficiencies():
+    g = golden("fa3_efficiency.json")
+    for s, e in g["efficiency"].items():
+        assert round(P.wave_efficiency(g["work"], int(s), g["sms"]), g["printed_precision"]) == e
+
+
+def test_overhead_ratio_matches_page():
+    g = golden("split_table.json")["overhead_check"]
+    # g = 1, fp16, D large: 4 S g (D+2) / (L D elt) -> 2S/t as D grows
+    r = P.workspace_ratio(g["splits"], 1, 1 << 20, 2, g["tokens"])
+    assert abs(100 * r - g["ratio_percent_approx"]) < 0.01
+    assert abs(r - 2 * g["splits"] / g["tokens"]) < 1e-9
+
+
+def test_traffic_rule_reduces_to_page_rule():
+    for work in (1, 3, 8, 32, 128, 500):
+        for n_blocks in (1, 2, 3, 7, 100, 1000):
+            a = P.num_splits_fa2(work, 264, n_blocks, 128)
+            b = P.num_splits_traffic(work, 264, n_blocks, 128, 8, 128, 2, 10**9, 1e9)
+            assert a == b
+
+
+def test_rule_invariants():
+    for work in (1, 2, 8, 64, 409, 410, 512, 4096):
+        for n_blocks in (0, 1, 5, 64, 1000):
+            for slots in (264, 512, 768):
+                s = P.num_splits_traffic(work, slots, n_blocks, 128, 4, 128, 2, 128 * max(n_blocks, 1), 0.05)
+                assert s >= 1
+                if work >= 0.8 * slots or n_blocks <= 1:
+                    assert s == 1
+                assert s <= max(1, min(128, slots, n_blocks))
+                if s > 1:
+                    assert math.ceil(n_blocks / s) != math.ceil(n_blocks / (s - 1))
+                    assert P.workspace_ratio(s, 4, 128, 2, 128 * n_blocks) <= 0.05
+
+
+def test_chunk_for():
+    assert P.chunk_for(1000, 8, 1) == 125
+    assert P.chunk_for(1000, 3, 1) == 334
+    assert P.chunk_for(128000, 56, 128) == 2304
+    assert P.chunk_for(0, 4, 16) == 16
