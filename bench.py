@@ -1,0 +1,247 @@
+"""Decode-attention benchmark: one layer-step of split-KV decode on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
+
+A step is the whole hot path for one batch: fd_decode_split (split kernel)
+then fd_merge (merge kernel), back to back on one stream, inputs already
+resident in HBM (the plan is made once, outside the timed region). K/V live in
+several seeded copies that the steps rotate through, together larger than
+twice the 256 MB Infinity Cache, so no step is served from the previous one.
+
+Prints ONE JSON line: value = achieved K/V bandwidth in TB/s (algorithmic
+K+V bytes of the step / wall time per step), the microseconds per layer-step,
+a roofline object for the split kernel (its average duration from HIP events
+recorded on the launch stream) and the float64 CPU oracle timed on the host
+over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 << 20      # Infinity Cache
+
+WORKLOADS = {
+    # name: (builder kwargs, description)
+    "gqa64x8_f16_L128000": "B=1, 64 query heads over 8 KV heads, D=128, L=128000, fp16, planner's split count",
+    "mha32_bf16_L65536_C1024": "B=1, 32 = 32 heads, D=128, L=65536, bf16, 1024-token chunks, (o, LSE) workspace",
+    "paged_gqa32x8_f16_B16": "B=16, 32 query heads over 8 KV heads, D=128, L ~ U[1024, 32768], fp16, 16-token pages",
+    "edge_gqa32x8_f16_B64": "B=64, 32 query heads over 8 KV heads, D=128, L ~ U[1, 2048], fp16, K x 8",
+    "tiny_mha_f32_L1000": "B=1, 4 = 4 heads, D=64, L=1000, fp32, 3 splits",
+}
+
+
+def make_workload(name: str, device):
+    import fd_workloads as W
+
+    builders = {
+        "gqa64x8_f16_L128000": lambda: W.long_gqa_f16(device=device),
+        "mha32_bf16_L65536_C1024": lambda: W.mha_bf16_chunked(device=device),
+        "paged_gqa32x8_f16_B16": lambda: W.paged_ragged_f16(device=device),
+        "edge_gqa32x8_f16_B64": lambda: W.edge_gqa_f16(device=device),
+        "tiny_mha_f32_L1000": lambda: W.tiny_mha_f32(num_splits=3, device=device),
+    }
+    if name not in builders:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(builders)}")
+    return builders[name]()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_fd_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kernel_hash: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_split_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, max_heads: int):
+    """Time the float64 oracle on the host over the first `max_heads` (b, hq)
+    pairs of copy 0 and scale to the whole step; returns the JSON object."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    from oracle import attention as A
+
+    cpu = w.to("cpu")
+    cache = A.Cache(cpu.q, cpu.k, cpu.v, cpu.seq_lens, cpu.block_table)
+    pairs = [(b, h) for b in range(cache.B) for h in range(cache.Hq)][:max_heads]
+    A.attention_one(cache, *pairs[0])                       # warm the allocator
+    t0 = time.perf_counter()
+    out = [A.attention_one(cache, b, h) for b, h in pairs]
+    dt = time.perf_counter() - t0
+    # KV bytes the sampled heads stand for, out of the step's total
+    lens = cpu.seq_lens.to(torch.int64).tolist()
+    per_head_bytes = [lens[b] * 2 * cache.D * cpu.k.element_size() for b, _ in pairs]
+    sampled_fraction = sum(per_head_bytes) / (sum(lens) * cache.Hq * 2 * cache.D * cpu.k.element_size())
+    step_s = dt / max(sampled_fraction, 1e-12)
+    kv_bytes = w.kv_bytes()
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [torch.get_num_threads()])
+    return {
+        "value": kv_bytes / step_s / 1e12, "unit": "TB/s", "us_per_step": step_s * 1e6, "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(pairs)} of {cache.B * cache.Hq} (sequence, query head) outputs of copy 0 in float64 "
+                  f"({dt:.1f} s), scaled by their share of the step's KV bytes ({sampled_fraction:.3f})",
+    }, out, pairs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa64x8_f16_L128000", choices=sorted(WORKLOADS))
+    ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = planner)")
+    ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate (0 = enough for 2x the MALL)")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs the decode on a single device "
+              "(sharding across GPUs is a design note, not built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_fd_amd as fd
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {args.workload}: {WORKLOADS[args.workload]}", file=sys.stderr, flush=True)
+
+    w0 = make_workload(args.workload, dev)
+    step_kv = w0.kv_bytes()
+    alloc = w0.k.numel() * w0.k.element_size() * 2
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / step_kv) + 1)
+    import fd_workloads as W
+
+    ws = [w0] + [W.redraw_kv(w0, 7000 + i) for i in range(1, copies)]
+    torch.cuda.synchronize()
+
+    opts = {"ws_format": w0.ws_format}
+    if args.splits:
+        opts["force_splits"] = args.splits
+    elif w0.num_splits:
+        opts["force_splits"] = w0.num_splits
+    if w0.chunk_tokens and not args.splits:
+        opts["force_chunk_tokens"] = w0.chunk_tokens
+    prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
+    t0 = time.perf_counter()
+    plan = fd.fd_plan(prob, **opts)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    ws_o, ws_stats = fd.workspace(plan, dev)
+    out = torch.empty(w0.batch, w0.num_q_heads, w0.head_dim, dtype=torch.float32, device=dev)
+    lse = torch.empty(w0.batch, w0.num_q_heads, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        w = ws[i % copies]
+        if evs is not None:
+            evs[0].record(stream)
+        fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, wall clock between synchronisations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_step = wall / args.steps * 1e6
+
+    # per-kernel durations: same steps again with events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    split_us = sum(split_ms) / len(split_ms) * 1e3
+    merge_us = sum(merge_ms) / len(merge_ms) * 1e3
+
+    tbps = step_kv / (us_step * 1e-6) / 1e12
+    achieved = step_kv / (split_us * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    traffic = traffic_from_profile(args.workload, khash)
+    result = {
+        "metric": "decode-attention µs/layer-step and achieved HBM TB/s (% of peak), B=1 L=128k GQA",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 5),
+        "us_per_layer_step": round(us_step, 2),
+        "pct_of_peak": round(100 * tbps * 1e3 / PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[w0.k.dtype],
+        "data": "synthetic: seeded N(0,1) q/K/V",
+        "config": {
+            "workload": args.workload, "batch": w0.batch, "q_heads": w0.num_q_heads, "kv_heads": w0.num_kv_heads,
+            "head_dim": w0.head_dim, "max_seq_len": w0.max_seq_len, "kv_bytes_per_step": step_kv,
+            "kv_bytes_allocated": alloc, "kv_copies": copies, "layout": "paged" if w0.paged else "contiguous",
+            "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
+            "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
+            "slots": plan.slots, "plan_us": round(plan_us, 1),
+        },
+        "split_kernel_us": round(split_us, 2),
+        "merge_kernel_us": round(merge_us, 2),
+        "merge_share": round(merge_us / max(split_us + merge_us, 1e-9), 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": "split", "bytes_per_launch": step_kv, "kernel_source_hash": khash,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
+        cb, ref, pairs = cpu_baseline(w0, args.cpu_heads)
+        # the GPU output of copy 0 on the sampled pairs, against the oracle (sanity)
+        step(0)
+        torch.cuda.synchronize()
+        import numpy as np
+
+        o = out.cpu().double().numpy()
+        err = max(float(np.abs(o[b, h] - r[0]).max()) for (b, h), r in zip(pairs, ref))
+        cb["gpu_max_abs_err_on_sample"] = err
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

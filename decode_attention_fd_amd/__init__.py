@@ -1,0 +1,236 @@
+"""Python binding of the split-KV decode-attention library ``libfd.so``.
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+behind the C ABI of ``include/fd.h``. The entry points keep the C names:
+
+    plan = fd_plan(problem_for(q, k, v, seq_lens, ...), **options)
+    ws_o, ws_stats = workspace(plan, device)
+    fd_decode_split(plan, q, k, v, seq_lens, ws_o, ws_stats, block_table=None)
+    fd_merge(plan, ws_o, ws_stats, out, lse)
+
+``flash_decode`` chains the three for convenience. PyTorch provides device
+memory and the stream (``torch.cuda.current_stream()``); nothing here computes.
+If ``libfd.so`` is missing every entry point raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfd.so")
+
+FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_ALIGNMENT, FD_ERR_WORKSPACE, FD_ERR_HIP, FD_ERR_BAD_PLAN = range(7)
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+LAYOUT_CONTIGUOUS, LAYOUT_PAGED = 0, 1
+WS_FORMATS = {"uml": 0, "olse": 1}
+KERNELS = {"auto": 0, "mfma": 1, "valu": 2}
+HEURISTICS = {"mi355x": 0, "fa2": 1}
+PLAN_MAGIC = 0x46445031
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_t", ctypes.c_int64),
+        ("kv_capacity", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("bt_stride_b", ctypes.c_int64),
+        ("pool_stride_page", ctypes.c_int64), ("pool_stride_t", ctypes.c_int64), ("pool_stride_h", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+    ]
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [
+        ("num_cus", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+        ("force_chunk_tokens", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("kernel", ctypes.c_int32),
+        ("heuristic", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("overhead_budget", ctypes.c_float),
+        ("reserved", ctypes.c_int32 * 7),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("num_splits", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+        ("kernel", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("tile_tokens", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("slots", ctypes.c_int32),
+        ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("reserved1", ctypes.c_int32),
+        ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64),
+        ("prob", Problem), ("checksum", ctypes.c_uint64),
+    ]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p)]
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {status_str(status)} (status {status})"
+        if status == FD_ERR_HIP:
+            msg += f" [{lib().fd_last_hip_error().decode()}]"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libfd.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_fd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fd_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), ctypes.POINTER(Plan)]
+        L.fd_plan.restype = ctypes.c_int
+        L.fd_decode_split.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.fd_decode_split.restype = ctypes.c_int
+        L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
+        L.fd_merge.restype = ctypes.c_int
+        L.fd_status_str.argtypes = [ctypes.c_int]
+        L.fd_status_str.restype = ctypes.c_char_p
+        L.fd_last_hip_error.argtypes = []
+        L.fd_last_hip_error.restype = ctypes.c_char_p
+        L.fd_version.argtypes = []
+        L.fd_version.restype = ctypes.c_char_p
+        L.fd_struct_size.argtypes = [ctypes.c_int]
+        L.fd_struct_size.restype = ctypes.c_size_t
+        for i, cls in enumerate((Problem, PlanOpts, Plan, Args)):
+            if L.fd_struct_size(i) != ctypes.sizeof(cls):
+                raise RuntimeError(f"ABI mismatch for {cls.__name__}: C {L.fd_struct_size(i)} vs {ctypes.sizeof(cls)}")
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fd_status_str(status).decode()
+
+
+def version() -> str:
+    return lib().fd_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FD_OK:
+        raise FdError(status, where)
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def problem_for(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None,
+                scale: float = 0.0) -> Problem:
+    """Describe a decode step from its tensors (shapes and strides only).
+
+    q [B, Hq, D]; contiguous K/V [B, Hkv, T, D] or paged pools [P, page, Hkv, D]
+    with ``block_table`` int32 [B, max_pages]. ``max_seq_len`` defaults to
+    ``seq_lens.max()`` (a device sync if seq_lens lives on the GPU)."""
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("K and V must have the same shape and strides")
+    if k.dtype not in DTYPES or q.dtype not in DTYPES:
+        raise ValueError(f"unsupported dtype {k.dtype}/{q.dtype}")
+    p = Problem()
+    p.batch, p.num_q_heads, p.head_dim = q.shape
+    p.q_dtype = DTYPES[q.dtype]
+    p.kv_dtype = DTYPES[k.dtype]
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    if q.stride(2) != 1 or k.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    p.max_seq_len = int(max_seq_len)
+    p.scale = float(scale)
+    if block_table is None:
+        p.layout = LAYOUT_CONTIGUOUS
+        p.num_kv_heads = k.shape[1]
+        p.kv_stride_b, p.kv_stride_h, p.kv_stride_t = k.stride(0), k.stride(1), k.stride(2)
+        p.kv_capacity = k.shape[2]
+    else:
+        p.layout = LAYOUT_PAGED
+        p.num_kv_heads = k.shape[2]
+        p.num_pages, p.page_size = k.shape[0], k.shape[1]
+        p.pool_stride_page, p.pool_stride_t, p.pool_stride_h = k.stride(0), k.stride(1), k.stride(2)
+        p.max_pages_per_seq = block_table.shape[1]
+        p.bt_stride_b = block_table.stride(0)
+        if block_table.dtype != torch.int32 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be int32 with contiguous rows")
+    return p
+
+
+def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_splits: int = 0,
+            force_chunk_tokens: int = 0, ws_format: str = "uml", kernel: str = "auto",
+            heuristic: str = "mi355x", max_splits: int = 0, overhead_budget: float = 0.0) -> Plan:
+    """Call ``fd_plan``. ``num_cus=0`` asks the current device."""
+    o = PlanOpts()
+    o.num_cus, o.wgs_per_cu = num_cus, wgs_per_cu
+    o.force_splits, o.force_chunk_tokens = force_splits, force_chunk_tokens
+    o.ws_format = WS_FORMATS[ws_format]
+    o.kernel = KERNELS[kernel]
+    o.heuristic = HEURISTICS[heuristic]
+    o.max_splits = max_splits
+    o.overhead_budget = overhead_budget
+    plan = Plan()
+    _check(lib().fd_plan(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(plan)), "fd_plan")
+    return plan
+
+
+def workspace(plan: Plan, device) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate the fp32 workspace the plan asks for: (ws_o [B,Hq,S,D], ws_stats)."""
+    pr = plan.prob
+    S, D = plan.num_splits, pr.head_dim
+    ws_o = torch.empty(pr.batch, pr.num_q_heads, S, D, dtype=torch.float32, device=device)
+    last = 2 if plan.ws_format == WS_FORMATS["uml"] else 1
+    ws_stats = torch.empty(pr.batch, pr.num_q_heads, S, last, dtype=torch.float32, device=device)
+    return ws_o, ws_stats
+
+
+def fd_decode_split(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, block_table=None, stream=None) -> None:
+    """Launch the split kernel on ``stream`` (default: torch's current stream)."""
+    a = Args(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_table))
+    st = lib().fd_decode_split(ctypes.byref(plan), ctypes.byref(a), _ptr(ws_o), ws_o.numel() * ws_o.element_size(),
+                               _ptr(ws_stats), ws_stats.numel() * ws_stats.element_size(), _stream_handle(stream))
+    _check(st, "fd_decode_split")
+
+
+def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:
+    """Launch the merge kernel: out [B,Hq,D] fp32 (contiguous), lse [B,Hq] fp32 or None."""
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor")
+    st = lib().fd_merge(ctypes.byref(plan), _ptr(ws_o), _ptr(ws_stats), _ptr(out), _ptr(lse),
+                        _stream_handle(stream))
+    _check(st, "fd_merge")
+
+
+def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,
+                 return_lse: bool = True, stream=None, **plan_options):
+    """Plan, split and merge in one call; returns (out, lse) fp32 (lse None if not asked)."""
+    plan = fd_plan(problem_for(q, k, v, seq_lens, block_table, max_seq_len, scale), **plan_options)
+    ws_o, ws_stats = workspace(plan, q.device)
+    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device) if return_lse else None
+    fd_decode_split(plan, q, k, v, seq_lens, ws_o, ws_stats, block_table, stream)
+    fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+    return out, lse

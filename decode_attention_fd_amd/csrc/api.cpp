@@ -1,0 +1,221 @@
+// The C ABI: argument validation, device queries for the planner, and the
+// launches of the split and merge kernels on the caller's stream.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+
+int valu_tile_tokens(int head_dim, int kv_dtype);          // split_valu.hip
+int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int* out);
+int occupancy_split_valu(int head_dim, int kv_dtype, int layout, int group_tpl, int* out);
+
+int occupancy_split(int kernel, int head_dim, int kv_dtype, int layout, int group_tpl, int* out) {
+  if (kernel == FD_KERNEL_MFMA) return occupancy_split_mfma(head_dim, kv_dtype, layout, out);
+  return occupancy_split_valu(head_dim, kv_dtype, layout, group_tpl, out);
+}
+
+int split_tile_tokens(int kernel, int head_dim, int kv_dtype) {
+  return kernel == FD_KERNEL_MFMA ? 32 : valu_tile_tokens(head_dim, kv_dtype);
+}
+
+int split_waves_per_wg(int /*kernel*/) { return 4; }
+
+// Resident split workgroups per CU of each compiled variant, generated at build
+// time from the compiler's resource usage (VGPRs and LDS per workgroup); used
+// when the planner runs without a device. tests/test_gpu_parity.py checks it
+// against hipOccupancyMaxActiveBlocksPerMultiprocessor on the device.
+namespace {
+struct OccRow {
+  int kernel, head_dim, kv_dtype, group_tpl, paged, wgs;
+};
+const OccRow kOccupancy[] = {
+#include "fd_occupancy.inc"
+};
+}  // namespace
+
+int default_wgs_per_cu(int kernel, int head_dim, int kv_dtype, int group_tpl, int layout) {
+  const int paged = layout == FD_LAYOUT_PAGED;
+  for (const OccRow& r : kOccupancy)
+    if (r.kernel == kernel && r.head_dim == head_dim && r.kv_dtype == kv_dtype && r.paged == paged &&
+        (kernel == FD_KERNEL_MFMA || r.group_tpl == group_tpl))
+      return r.wgs;
+  return 1;
+}
+
+namespace {
+
+thread_local char g_last_hip[256] = "";
+
+int hip_fail(int err, const char* where) {
+  snprintf(g_last_hip, sizeof(g_last_hip), "%s: %s (%d)", where,
+           hipGetErrorString((hipError_t)err), err);
+  return FD_ERR_HIP;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_plan(const fd_plan_t* plan) {
+  if (!plan) return FD_ERR_INVALID_ARG;
+  if (plan->magic != FD_PLAN_MAGIC || plan->checksum != plan_checksum(plan)) return FD_ERR_BAD_PLAN;
+  if (validate_problem(&plan->prob) != FD_OK) return FD_ERR_BAD_PLAN;
+  if (plan->num_splits < 1 || plan->chunk_tokens < 1) return FD_ERR_BAD_PLAN;
+  return FD_OK;
+}
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+}  // namespace
+}  // namespace fd
+
+using namespace fd;
+
+extern "C" {
+
+FD_API const char* fd_version(void) { return FD_VERSION_STRING; }
+
+FD_API const char* fd_status_str(int status) {
+  switch (status) {
+    case FD_OK: return "ok";
+    case FD_ERR_INVALID_ARG: return "invalid argument";
+    case FD_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, group size or layout";
+    case FD_ERR_ALIGNMENT: return "pointer or row stride not 16-byte aligned";
+    case FD_ERR_WORKSPACE: return "workspace smaller than the plan requires";
+    case FD_ERR_HIP: return "HIP call or kernel launch failed";
+    case FD_ERR_BAD_PLAN: return "plan not produced by fd_plan or modified since";
+    default: return "unknown status";
+  }
+}
+
+FD_API const char* fd_last_hip_error(void) { return g_last_hip; }
+
+FD_API size_t fd_struct_size(int which) {
+  switch (which) {
+    case 0: return sizeof(fd_problem);
+    case 1: return sizeof(fd_plan_opts);
+    case 2: return sizeof(fd_plan_t);
+    case 3: return sizeof(fd_args);
+    default: return 0;
+  }
+}
+
+FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* out) {
+  if (!prob || !out) return FD_ERR_INVALID_ARG;
+  fd_plan_opts o;
+  memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.num_cus < 0 || o.wgs_per_cu < 0) return FD_ERR_INVALID_ARG;
+  int st = validate_problem(prob);
+  if (st != FD_OK) return st;
+  const int kernel = choose_kernel(prob, o.kernel);
+  if (kernel < 0) return -kernel;
+  const int gtpl = valu_group_template(prob->num_q_heads / prob->num_kv_heads);
+  if (o.num_cus == 0) {
+    int dev = 0, n = 0;
+    int err = (int)hipGetDevice(&dev);
+    if (err) return hip_fail(err, "hipGetDevice");
+    err = (int)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err) return hip_fail(err, "hipDeviceGetAttribute");
+    o.num_cus = n;
+    if (o.wgs_per_cu == 0) {
+      int occ = 0;
+      err = occupancy_split(kernel, prob->head_dim, prob->kv_dtype, prob->layout, gtpl, &occ);
+      if (err) return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+      o.wgs_per_cu = occ > 0 ? occ : 1;
+    }
+  }
+  if (o.wgs_per_cu == 0)
+    o.wgs_per_cu = default_wgs_per_cu(kernel, prob->head_dim, prob->kv_dtype, gtpl, prob->layout);
+  o.kernel = kernel;
+  return plan_core(prob, &o, out);
+}
+
+FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes,
+                           float* ws_stats, size_t ws_stats_bytes, void* stream) {
+  int st = check_plan(plan);
+  if (st != FD_OK) return st;
+  if (!args || !args->q || !args->k || !args->v || !args->seq_lens || !ws_o || !ws_stats)
+    return FD_ERR_INVALID_ARG;
+  const fd_problem& pr = plan->prob;
+  const bool paged = pr.layout == FD_LAYOUT_PAGED;
+  if (paged && !args->block_table) return FD_ERR_INVALID_ARG;
+  if (!aligned(args->q, 16) || !aligned(args->k, 16) || !aligned(args->v, 16) || !aligned(args->seq_lens, 4) ||
+      (paged && !aligned(args->block_table, 4)) || !aligned(ws_o, 16) || !aligned(ws_stats, 8))
+    return FD_ERR_ALIGNMENT;
+  if (ws_o_bytes < (size_t)plan->ws_o_bytes || ws_stats_bytes < (size_t)plan->ws_stats_bytes)
+    return FD_ERR_WORKSPACE;
+
+  SplitParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = args->q;
+  p.k = args->k;
+  p.v = args->v;
+  p.seq_lens = args->seq_lens;
+  p.block_table = paged ? args->block_table : nullptr;
+  p.ws_o = ws_o;
+  p.ws_stats = ws_stats;
+  p.q_sb = pr.q_stride_b;
+  p.q_sh = pr.q_stride_h;
+  p.kv_sb = pr.kv_stride_b;
+  p.kv_sh = pr.kv_stride_h;
+  p.kv_st = pr.kv_stride_t;
+  p.pool_sp = pr.pool_stride_page;
+  p.pool_st = pr.pool_stride_t;
+  p.pool_sh = pr.pool_stride_h;
+  p.bt_sb = pr.bt_stride_b;
+  p.B = pr.batch;
+  p.Hq = pr.num_q_heads;
+  p.Hkv = pr.num_kv_heads;
+  p.g = plan->group;
+  p.S = plan->num_splits;
+  p.chunk = plan->chunk_tokens;
+  if (paged) {
+    p.cap_tokens = pr.max_pages_per_seq * pr.page_size;
+    p.page_log2 = ilog2(pr.page_size);
+    p.num_pages = pr.num_pages;
+  } else {
+    p.cap_tokens = pr.kv_capacity;
+  }
+  // Splits past S*chunk are never launched: clamp there as well.
+  const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;
+  if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
+  p.ws_format = plan->ws_format;
+  p.scale_log2 = (float)((double)plan->scale * 1.4426950408889634);
+
+  int err;
+  if (plan->kernel == FD_KERNEL_MFMA)
+    err = launch_split_mfma(p, pr.head_dim, pr.kv_dtype, pr.layout, stream);
+  else
+    err = launch_split_valu(p, pr.head_dim, pr.kv_dtype, pr.layout, valu_group_template(plan->group), stream);
+  if (err) return hip_fail(err, "split kernel launch");
+  return FD_OK;
+}
+
+FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats, float* out, float* lse,
+                    void* stream) {
+  int st = check_plan(plan);
+  if (st != FD_OK) return st;
+  if (!ws_o || !ws_stats || !out) return FD_ERR_INVALID_ARG;
+  if (!aligned(ws_o, 16) || !aligned(ws_stats, 8) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return FD_ERR_ALIGNMENT;
+  MergeParams p;
+  p.ws_o = ws_o;
+  p.ws_stats = ws_stats;
+  p.out = out;
+  p.lse = lse;
+  p.BH = plan->prob.batch * plan->prob.num_q_heads;
+  p.S = plan->num_splits;
+  p.ws_format = plan->ws_format;
+  int err = launch_merge(p, plan->prob.head_dim, stream);
+  if (err) return hip_fail(err, "merge kernel launch");
+  return FD_OK;
+}
+
+}  // extern "C"

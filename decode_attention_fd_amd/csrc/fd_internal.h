@@ -1,0 +1,66 @@
+// Internal interface between the host API (api.cpp), the planner (plan.cpp)
+// and the HIP kernels (split_mfma.hip, split_valu.hip, merge.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include "fd.h"
+
+namespace fd {
+
+// Everything one split-kernel launch needs, passed by value. Strides are in
+// elements, as in fd_problem.
+struct SplitParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  float* ws_o;
+  float* ws_stats;
+  int64_t q_sb, q_sh;
+  int64_t kv_sb, kv_sh, kv_st;          // contiguous
+  int64_t pool_sp, pool_st, pool_sh;    // paged
+  int64_t bt_sb;
+  int32_t B, Hq, Hkv, g;
+  int32_t S, chunk;
+  int32_t cap_tokens;                   // seq_lens are clamped to [0, cap_tokens]
+  int32_t page_log2, num_pages;
+  int32_t ws_format;
+  float scale_log2;                     // scale * log2(e): scores go straight to base 2
+};
+
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_stats;
+  float* out;
+  float* lse;
+  int32_t BH, S, ws_format;
+};
+
+// Launchers: return the HIP status of the launch (hipSuccess == 0).
+int launch_split_mfma(const SplitParams& p, int head_dim, int kv_dtype, int layout, void* stream);
+int launch_split_valu(const SplitParams& p, int head_dim, int kv_dtype, int layout, int group_tpl,
+                      void* stream);
+int launch_merge(const MergeParams& p, int head_dim, void* stream);
+
+// Per-kernel geometry the planner needs (tokens per wave tile, waves per
+// workgroup) and the compiled resident-workgroups-per-CU of each variant.
+int split_tile_tokens(int kernel, int head_dim, int kv_dtype);
+int split_waves_per_wg(int kernel);
+int valu_group_template(int g);                 // 1, 2 or 4; 0 if unsupported
+int default_wgs_per_cu(int kernel, int head_dim, int kv_dtype, int group_tpl, int layout);
+
+// The pure host planner (no HIP calls). opts must be fully resolved:
+// num_cus > 0 and wgs_per_cu > 0.
+int plan_core(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* out);
+int validate_problem(const fd_problem* prob);
+int choose_kernel(const fd_problem* prob, int requested);
+uint64_t plan_checksum(const fd_plan_t* plan);
+
+// Element size of an fd_dtype, 0 if invalid.
+inline int dtype_size(int dt) {
+  return dt == FD_DTYPE_F32 ? 4 : (dt == FD_DTYPE_F16 || dt == FD_DTYPE_BF16) ? 2 : 0;
+}
+
+}  // namespace fd

@@ -1,0 +1,217 @@
+// Host planner: problem validation, kernel choice and the split-count rule.
+// Pure C++ (no HIP calls), so it runs and is tested without a GPU.
+//
+// The split-count rule is the wave-efficiency rule of "Flash-Decoding:
+// Split-KV Attention for Long-Context Decode" (kanthi.in) §6: S = 1 when the
+// work units already fill 80 % of the resident slots; otherwise, among split
+// counts that change the number of blocks per split, the smallest whose
+// last-wave efficiency reaches 85 % of the best. The MI355X variant counts
+// slots as CUs x resident split workgroups per CU, counts blocks in units of
+// one workgroup iteration, and drops split counts whose fp32 workspace
+// traffic (written by the split kernel and read back by the merge) exceeds a
+// budget of the KV bytes -- the overhead check at the end of §6, generalised
+// to g query heads per KV head.
+#include <math.h>
+#include <string.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+
+namespace {
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool eligible(int s, int64_t n_blocks) {
+  return s == 1 || cdiv64(n_blocks, s) != cdiv64(n_blocks, s - 1);
+}
+
+double wave_eff(int64_t work, int s, int64_t slots) {
+  double w = (double)work * (double)s / (double)slots;
+  return w / ceil(w);
+}
+
+double ws_ratio(int s, int g, int d, int elt, int64_t max_len) {
+  if (max_len <= 0) return INFINITY;
+  return (2.0 * s * g * (d + 2) * 4.0) / (2.0 * (double)max_len * d * elt);
+}
+
+// kanthi.in §6 rule; with budget < 0 no traffic bound is applied.
+int split_rule(int64_t work, int64_t slots, int64_t n_blocks, int max_splits, int g, int d, int elt,
+               int64_t max_len, double budget) {
+  if ((double)work >= 0.8 * (double)slots) return 1;
+  int64_t cap = max_splits;
+  if (slots < cap) cap = slots;
+  if (n_blocks < cap) cap = n_blocks;
+  if (cap <= 1) return 1;
+  double best = 0.0;
+  for (int s = 1; s <= cap; ++s) {
+    if (!eligible(s, n_blocks)) continue;
+    if (s > 1 && budget >= 0.0 && ws_ratio(s, g, d, elt, max_len) > budget) continue;
+    double e = wave_eff(work, s, slots);
+    if (e > best) best = e;
+  }
+  for (int s = 1; s <= cap; ++s) {
+    if (!eligible(s, n_blocks)) continue;
+    if (s > 1 && budget >= 0.0 && ws_ratio(s, g, d, elt, max_len) > budget) continue;
+    if (wave_eff(work, s, slots) >= 0.85 * best) return s;
+  }
+  return 1;
+}
+
+}  // namespace
+
+int validate_problem(const fd_problem* p) {
+  if (!p) return FD_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1) return FD_ERR_INVALID_ARG;
+  if (p->num_q_heads % p->num_kv_heads) return FD_ERR_INVALID_ARG;
+  if (p->batch > 65535 || p->num_kv_heads > 65535) return FD_ERR_UNSUPPORTED;
+  if (dtype_size(p->q_dtype) == 0 || dtype_size(p->kv_dtype) == 0) return FD_ERR_INVALID_ARG;
+  if (p->layout != FD_LAYOUT_CONTIGUOUS && p->layout != FD_LAYOUT_PAGED) return FD_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return FD_ERR_UNSUPPORTED;
+  if (p->q_dtype != p->kv_dtype) return FD_ERR_UNSUPPORTED;
+  if (p->max_seq_len < 0) return FD_ERR_INVALID_ARG;
+  if (!(isfinite(p->scale))) return FD_ERR_INVALID_ARG;
+  const int64_t elt = dtype_size(p->kv_dtype);
+  const int64_t D = p->head_dim;
+  if (p->q_stride_h < D || p->q_stride_b < 0) return FD_ERR_INVALID_ARG;
+  if ((p->q_stride_h * elt) % 16 || (p->q_stride_b * elt) % 16) return FD_ERR_ALIGNMENT;
+  if (p->layout == FD_LAYOUT_CONTIGUOUS) {
+    if (p->kv_stride_t < D || p->kv_stride_h < 0 || p->kv_stride_b < 0) return FD_ERR_INVALID_ARG;
+    if (p->kv_capacity < p->max_seq_len || p->kv_capacity < 0) return FD_ERR_INVALID_ARG;
+    if ((p->kv_stride_t * elt) % 16 || (p->kv_stride_h * elt) % 16 || (p->kv_stride_b * elt) % 16)
+      return FD_ERR_ALIGNMENT;
+  } else {
+    if (!is_pow2(p->page_size) || p->page_size < 16 || p->page_size > (1 << 20)) return FD_ERR_UNSUPPORTED;
+    if (p->num_pages < 1 || p->max_pages_per_seq < 1 || p->bt_stride_b < 0) return FD_ERR_INVALID_ARG;
+    if ((int64_t)p->max_pages_per_seq * p->page_size < p->max_seq_len) return FD_ERR_INVALID_ARG;
+    if ((int64_t)p->max_pages_per_seq * p->page_size > (int64_t)0x7fffffff) return FD_ERR_UNSUPPORTED;
+    if (p->pool_stride_t < D || p->pool_stride_page < 0 || p->pool_stride_h < 0) return FD_ERR_INVALID_ARG;
+    if ((p->pool_stride_t * elt) % 16 || (p->pool_stride_page * elt) % 16 || (p->pool_stride_h * elt) % 16)
+      return FD_ERR_ALIGNMENT;
+  }
+  return FD_OK;
+}
+
+int valu_group_template(int g) {
+  if (g <= 1) return 1;
+  if (g <= 2) return 2;
+  if (g <= 4) return 4;
+  return 0;
+}
+
+int choose_kernel(const fd_problem* p, int requested) {
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const bool half = dtype_size(p->kv_dtype) == 2;
+  const bool mfma_ok = half && g <= 8;
+  const bool valu_ok = valu_group_template(g) != 0;
+  switch (requested) {
+    case FD_KERNEL_AUTO:
+      if (mfma_ok && g >= 2) return FD_KERNEL_MFMA;   // packed GQA: a dense enough contraction
+      if (valu_ok) return FD_KERNEL_VALU;
+      if (mfma_ok) return FD_KERNEL_MFMA;
+      return -FD_ERR_UNSUPPORTED;
+    case FD_KERNEL_MFMA:
+      return mfma_ok ? FD_KERNEL_MFMA : -FD_ERR_UNSUPPORTED;
+    case FD_KERNEL_VALU:
+      return valu_ok ? FD_KERNEL_VALU : -FD_ERR_UNSUPPORTED;
+    default:
+      return -FD_ERR_INVALID_ARG;
+  }
+}
+
+uint64_t plan_checksum(const fd_plan_t* plan) {
+  // FNV-1a over every byte before the checksum field.
+  const unsigned char* b = (const unsigned char*)plan;
+  const size_t n = offsetof(fd_plan_t, checksum);
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
+  if (!prob || !o || !out) return FD_ERR_INVALID_ARG;
+  int st = validate_problem(prob);
+  if (st != FD_OK) return st;
+  if (o->num_cus < 1 || o->wgs_per_cu < 1) return FD_ERR_INVALID_ARG;
+  if (o->force_splits < 0 || o->force_chunk_tokens < 0 || o->max_splits < 0) return FD_ERR_INVALID_ARG;
+  if (o->ws_format != FD_WS_UML && o->ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
+  if (o->heuristic != FD_HEURISTIC_MI355X && o->heuristic != FD_HEURISTIC_FA2) return FD_ERR_INVALID_ARG;
+  if (!(o->overhead_budget >= 0.0f)) return FD_ERR_INVALID_ARG;
+
+  const int kernel = choose_kernel(prob, o->kernel);
+  if (kernel < 0) return -kernel;
+
+  memset(out, 0, sizeof(*out));
+  const int g = prob->num_q_heads / prob->num_kv_heads;
+  const int elt = dtype_size(prob->kv_dtype);
+  const int D = prob->head_dim;
+  const int64_t max_len = prob->max_seq_len;
+  const int tile = split_tile_tokens(kernel, D, prob->kv_dtype);
+  const int waves = split_waves_per_wg(kernel);
+  const bool paged = prob->layout == FD_LAYOUT_PAGED;
+  // Paged addressing needs every wave tile inside one page run and tiles
+  // starting on page boundaries: chunks are multiples of max(page, tile).
+  const int64_t paged_align = paged ? (prob->page_size > tile ? prob->page_size : tile) : 1;
+
+  int64_t S = 1, chunk = 1;
+  int64_t slots = 0;
+  if (o->force_chunk_tokens > 0) {
+    chunk = o->force_chunk_tokens;
+    if (chunk % paged_align) return FD_ERR_INVALID_ARG;
+    S = o->force_splits > 0 ? o->force_splits : (max_len > 0 ? cdiv64(max_len, chunk) : 1);
+    if (S * chunk < max_len) return FD_ERR_INVALID_ARG;
+  } else if (o->force_splits > 0) {
+    S = o->force_splits;
+    chunk = cdiv64(max_len > 0 ? max_len : 1, S);
+    chunk = cdiv64(chunk, paged_align) * paged_align;
+  } else {
+    const int max_splits = o->max_splits > 0 ? o->max_splits : 128;
+    const int64_t work = (int64_t)prob->batch * prob->num_kv_heads;
+    int64_t block;
+    double budget;
+    if (o->heuristic == FD_HEURISTIC_FA2) {
+      slots = 2 * (int64_t)o->num_cus;
+      block = 128;
+      budget = -1.0;
+    } else {
+      slots = (int64_t)o->num_cus * o->wgs_per_cu;
+      block = (int64_t)tile * waves;
+      budget = o->overhead_budget > 0.0f ? (double)o->overhead_budget : 0.02;
+    }
+    const int64_t n_blocks = max_len > 0 ? cdiv64(max_len, block) : 0;
+    S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget);
+    int64_t align = block > paged_align ? block : paged_align;
+    if (paged && align % paged_align) align = paged_align;   // both are powers of two
+    chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
+    S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
+  }
+  if (S < 1 || S > 65535 || chunk < 1 || chunk > 0x7fffffff) return FD_ERR_UNSUPPORTED;
+  if (slots == 0) slots = (int64_t)o->num_cus * o->wgs_per_cu;
+
+  out->magic = FD_PLAN_MAGIC;
+  out->num_splits = (int32_t)S;
+  out->chunk_tokens = (int32_t)chunk;
+  out->kernel = kernel;
+  out->ws_format = o->ws_format;
+  out->group = g;
+  out->tile_tokens = tile;
+  out->waves_per_wg = waves;
+  out->slots = (int32_t)slots;
+  out->grid_x = (int32_t)S;
+  out->grid_y = prob->num_kv_heads;
+  out->grid_z = prob->batch;
+  out->scale = prob->scale != 0.0f ? prob->scale : (float)(1.0 / sqrt((double)D));
+  const int64_t heads = (int64_t)prob->batch * prob->num_q_heads;
+  out->ws_o_bytes = heads * S * D * 4;
+  out->ws_stats_bytes = heads * S * (o->ws_format == FD_WS_UML ? 2 : 1) * 4;
+  out->prob = *prob;
+  out->checksum = plan_checksum(out);
+  return FD_OK;
+}
+
+}  // namespace fd

@@ -1,0 +1,381 @@
+// Split kernel, packed-GQA tile on MFMA (gfx950), 16-bit K/V.
+//
+// One workgroup of 4 waves owns one (sequence b, KV head, split s) and the g
+// query heads that share the KV head ("Flash-Decoding: Split-KV Attention for
+// Long-Context Decode", kanthi.in, §1 GQA note: the query heads of a group are
+// the rows of one tile so each KV block is read once per group). The split is
+// [s*chunk, min(s*chunk + chunk, seq_len)) (§4 kernel 1). Its 32-token wave
+// tiles are dealt round-robin to the 4 waves; each wave runs its own fp32
+// online softmax (§4 kernel 1 loop; the recurrence of Milakov & Gimelshein)
+// with no barrier inside the loop, and the four wave states are merged once
+// at the end with the exact rescaled merge (§2 stable form).
+//
+// Per wave tile of 32 tokens:
+//   * K and V rows are fetched with fully coalesced 16-byte loads (a wave
+//     instruction reads whole rows; the address is one scalar base per
+//     instruction plus a constant lane offset) into registers, one tile ahead
+//     of use, and written to the wave's own LDS slice. Rows are padded by 16
+//     bytes so the 16 rows one MFMA operand read touches fall in distinct bank
+//     groups, while every LDS access is one base register plus an immediate.
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 tokens x 32 dims of
+//     K, B = 32 dims x 16 query columns. Columns 0..g-1 hold the g query heads;
+//     columns g..2g-1 hold the same heads again; the rest are zero.
+//   * Online softmax in base 2: x = (q.k) * scale * log2(e); the running max
+//     is exchanged across the four 16-lane groups; p = 2^(x - m).
+//   * O^T += V^T P^T on the same MFMA: the S^T accumulator layout is already
+//     the B-operand layout of P^T once the token order inside the 32-token
+//     k-block is permuted the same way on the V side, so P never leaves
+//     registers. On the V side each lane reads one contiguous D/8-byte slice
+//     of a token row; output block e then holds dims d = (D/16)*m + e, so one
+//     read feeds all D/16 MFMAs. P is split into a 16-bit high part (columns
+//     < g) and the 16-bit rounding of its remainder (columns g..2g-1); the two
+//     output columns are summed at the end, so P keeps ~22 (f16) / ~16 (bf16)
+//     bits. The row sum l is accumulated from the unrounded fp32 p.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct Mma;
+template <> struct Mma<_Float16> {
+  typedef f16x8 vec;
+  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<__bf16> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int NW = 4;    // waves per workgroup
+constexpr int TT = 32;   // tokens per wave tile
+constexpr float LN2 = 0.69314718055994530942f;
+
+template <int D> struct Geo {
+  static constexpr int ROWB = D * 2;        // bytes per K/V row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row (16 or 8)
+  static constexpr int RPI = 64 / CPR;      // rows per wave load instruction (4 or 8)
+  static constexpr int NI = TT / RPI;       // load instructions per tile per tensor (8 or 4)
+  static constexpr int ROWP = ROWB + 16;    // padded LDS row pitch
+  static constexpr int TILEB = TT * ROWP;   // bytes of one K (or V) tile in LDS
+  static constexpr int NDC = D / 32;        // QK^T k-blocks of 32 dims
+  static constexpr int NDB = D / 16;        // PV output blocks (dims d = NDB*m + e)
+  static constexpr int VW = NDB / 2;        // dwords of V one lane reads per token (4 or 2)
+};
+
+template <int N> struct VRead;
+template <> struct VRead<4> { typedef u32x4 type; };
+template <> struct VRead<2> { typedef u32x2 type; };
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Half `e & 1` of a and of b packed into one word (a's in the low half).
+__device__ __forceinline__ unsigned pick_half(unsigned a, unsigned b, int e) {
+  return (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+
+template <int D, typename T, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
+  using G = Geo<D>;
+  using V8 = typename Mma<T>::vec;
+  using VR = typename VRead<G::VW>::type;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NW][2][G::TILEB];
+  __shared__ float st_m[NW][16];
+  __shared__ float st_l[NW][16];
+
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = p.g;
+  const int col = lane & 15;     // MFMA column = query column
+  const int grp = lane >> 4;     // 16-lane group
+
+  int seq_len = p.seq_lens[b];
+  seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
+  const int start = s * p.chunk;
+  const int end = min(start + p.chunk, seq_len);
+  const int ntiles = end > start ? (end - start + TT - 1) / TT : 0;
+
+  // ---- Q^T as the B operand of S^T = K Q^T: column col holds head h(col).
+  const int hcol = col < g ? col : (col < 2 * g ? col - g : -1);
+  V8 qb[G::NDC];
+  {
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb +
+                    (int64_t)(kvh * g + (hcol < 0 ? 0 : hcol)) * p.q_sh;
+#pragma unroll
+    for (int c = 0; c < G::NDC; ++c) {
+      V8 v = *reinterpret_cast<const V8*>(qrow + 32 * c + 8 * grp);
+      qb[c] = hcol < 0 ? V8{} : v;
+    }
+  }
+
+  // ---- addressing: byte offsets, d contiguous
+  const char* kbase;
+  const char* vbase;
+  int64_t row_stride;                 // bytes between consecutive tokens (inside a page if paged)
+  int64_t page_stride = 0;
+  if (!PAGED) {
+    const int64_t off = ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh) * 2;
+    kbase = reinterpret_cast<const char*>(p.k) + off;
+    vbase = reinterpret_cast<const char*>(p.v) + off;
+    row_stride = p.kv_st * 2;
+  } else {
+    kbase = reinterpret_cast<const char*>(p.k) + (int64_t)kvh * p.pool_sh * 2;
+    vbase = reinterpret_cast<const char*>(p.v) + (int64_t)kvh * p.pool_sh * 2;
+    row_stride = p.pool_st * 2;
+    page_stride = p.pool_sp * 2;
+  }
+  const int lrow = lane / G::CPR;           // row of this lane inside a load instruction
+  const int lchunk = lane % G::CPR;         // 16-byte chunk of this lane
+  const uint32_t lane_off = (uint32_t)(lrow * row_stride) + lchunk * 16;
+  const int32_t* bt_row = PAGED ? p.block_table + (int64_t)b * p.bt_sb : nullptr;
+  const int page_mask = (1 << p.page_log2) - 1;
+
+  // Page id for load instruction `lane` of the tile starting at `t0` (lanes >= NI unused).
+  auto page_ids = [&](int t0) -> int {
+    int t = t0 + (lane < G::NI ? lane : 0) * G::RPI;
+    t = t < end - 1 ? t : end - 1;
+    int pid = bt_row[t >> p.page_log2];
+    pid = pid < 0 ? 0 : (pid >= p.num_pages ? p.num_pages - 1 : pid);
+    return pid;
+  };
+
+  u32x4 kr[G::NI], vr[G::NI];
+  // Loads of the tile starting at t0. Instruction i reads rows t0 + i*RPI + [0, RPI).
+  // Rows past `end` (tail tile only) re-read row end-1.
+  auto issue = [&](int t0, int pids) {
+    const bool full = t0 + TT <= end;               // wave-uniform
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+      const int ti = t0 + i * G::RPI;               // first row of the instruction (uniform)
+      const int tu = ti < end - 1 ? ti : end - 1;
+      int64_t ubase;                                // uniform byte offset of row tu
+      if (!PAGED) {
+        ubase = (int64_t)tu * row_stride;
+      } else {
+        const int pid = __builtin_amdgcn_readlane(pids, i);
+        ubase = (int64_t)pid * page_stride + (int64_t)(tu & page_mask) * row_stride;
+      }
+      uint32_t loff = lane_off;
+      if (!full) {
+        const int t = ti + lrow;
+        const int tc = t < end - 1 ? t : end - 1;
+        loff = (uint32_t)((tc - tu) * row_stride) + lchunk * 16;
+      }
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + ubase + loff);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + ubase + loff);
+    }
+  };
+
+  unsigned char* ldsK = lds[wave][0];
+  unsigned char* ldsV = lds[wave][1];
+
+  f32x4 oacc[G::NDB];
+#pragma unroll
+  for (int i = 0; i < G::NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max of x (base-2 scaled scores) for column col
+  float l_run = 0.f;         // this lane's share of the running sum
+  const float c2 = p.scale_log2;
+
+  int tile = wave;
+  int pid_cur = 0, pid_next = 0;
+  if (PAGED) {
+    if (tile < ntiles) pid_cur = page_ids(start + tile * TT);
+    if (tile + NW < ntiles) pid_next = page_ids(start + (tile + NW) * TT);
+  }
+  if (tile < ntiles) issue(start + tile * TT, pid_cur);
+
+  for (; tile < ntiles; tile += NW) {
+    const int t0 = start + tile * TT;
+    // registers -> padded LDS tile
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+      const int off = (i * G::RPI + lrow) * G::ROWP + lchunk * 16;
+      *reinterpret_cast<u32x4*>(ldsK + off) = kr[i];
+      *reinterpret_cast<u32x4*>(ldsV + off) = vr[i];
+    }
+    // next tile's loads go out before this tile's math
+    const int nt = tile + NW;
+    if (nt < ntiles) {
+      issue(start + nt * TT, pid_next);
+      if (PAGED && nt + NW < ntiles) pid_next = page_ids(start + (nt + NW) * TT);
+    }
+
+    // ---- S^T = K Q^T for tokens [0,16) and [16,32)
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < G::NDC; ++c) {
+        V8 a = *reinterpret_cast<const V8*>(ldsK + (tb * 16 + col) * G::ROWP + (4 * c + grp) * 16);
+        sacc[tb] = Mma<T>::run(a, qb[c], sacc[tb]);
+      }
+    }
+
+    // ---- online softmax (base 2). Lane holds tokens tb*16 + 4*grp + i.
+    float x[8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[tb * 4 + i] = sacc[tb][i] * c2;
+    if (t0 + TT > end) {                      // tail tile: mask rows past the split
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + tb * 16 + 4 * grp + i >= end) x[tb * 4 + i] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);    // finite: row t0 is always valid
+    if (__any(m_new > m_run)) {
+      const float alpha = exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < G::NDB; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    float pe[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = exp2_fast(x[e] - m_run);
+      psum += pe[e];
+    }
+    l_run += psum;
+
+    // ---- P^T as the B operand: high part in columns < g, remainder after.
+    V8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const T hi = (T)pe[e];
+      const float r = col < g ? pe[e] : pe[e] - (float)hi;
+      pb[e] = (T)r;
+    }
+
+    // ---- O^T += V^T P^T. k index j of group grp is token perm(8*grp + j):
+    // j < 4 -> 4*grp + j, j >= 4 -> 16 + 4*grp + (j - 4). Lane (grp, col) reads
+    // dims [NDB*col, NDB*col + NDB) of each of its 8 tokens.
+    VR w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = j < 4 ? 4 * grp + j : 16 + 4 * grp + (j - 4);
+      w[j] = *reinterpret_cast<const VR*>(ldsV + r * G::ROWP + col * (G::NDB * 2));
+    }
+#pragma unroll
+    for (int e = 0; e < G::NDB; ++e) {
+      u32x4 a;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) a[jj] = pick_half(w[2 * jj][e >> 1], w[2 * jj + 1][e >> 1], e);
+      oacc[e] = Mma<T>::run(__builtin_bit_cast(V8, a), pb, oacc[e]);
+    }
+  }
+
+  // ---- per-wave state -> LDS: ow[column][d], d = NDB*(4*grp + i) + e
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  float* ow = reinterpret_cast<float*>(lds[wave][0]);   // [16 columns][D] fp32 (<= TILEB bytes)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e4 = 0; e4 < G::NDB; e4 += 4) {
+      f32x4 v = {oacc[e4][i], oacc[e4 + 1][i], oacc[e4 + 2][i], oacc[e4 + 3][i]};
+      *reinterpret_cast<f32x4*>(ow + col * D + G::NDB * (4 * grp + i) + e4) = v;
+    }
+  if (grp == 0) {
+    st_m[wave][col] = m_run;
+    st_l[wave][col] = l_run;
+  }
+  __syncthreads();
+
+  // ---- merge the four wave states (exact rescale to the common max) and
+  // combine the high/low columns, then write the split's state.
+  const int Hq = p.Hq;
+  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, st_m[w2][h]);
+    float U = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float mw = st_m[w2][h];
+        const float a = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+        const float* o = reinterpret_cast<const float*>(lds[w2][0]);
+        U += a * (o[h * D + d] + o[(h + g) * D + d]);
+        L += a * st_l[w2][h];
+      }
+    }
+    const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + s;
+    if (p.ws_format == FD_WS_UML) {
+      p.ws_o[base * D + d] = U;
+      if (d == 0) {
+        p.ws_stats[base * 2] = M == -INFINITY ? -INFINITY : M * LN2;
+        p.ws_stats[base * 2 + 1] = L;
+      }
+    } else {
+      const bool empty = !(L > 0.f);
+      p.ws_o[base * D + d] = empty ? 0.f : U / L;
+      if (d == 0) p.ws_stats[base] = empty ? -INFINITY : (M + log2f(L)) * LN2;
+    }
+  }
+}
+
+template <int D, typename T, bool PAGED>
+int occupancy(int* out) {
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, split_mfma_kernel<D, T, PAGED>, NW * 64, 0);
+}
+
+template <int D, typename T, bool PAGED>
+int launch(const SplitParams& p, void* stream) {
+  dim3 grid(p.S, p.Hkv, p.B);
+  hipLaunchKernelGGL((split_mfma_kernel<D, T, PAGED>), grid, dim3(NW * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_split_mfma(const SplitParams& p, int head_dim, int kv_dtype, int layout, void* stream) {
+  const bool paged = layout == FD_LAYOUT_PAGED;
+  if (kv_dtype == FD_DTYPE_F16) {
+    if (head_dim == 128) return paged ? launch<128, _Float16, true>(p, stream) : launch<128, _Float16, false>(p, stream);
+    if (head_dim == 64) return paged ? launch<64, _Float16, true>(p, stream) : launch<64, _Float16, false>(p, stream);
+  } else if (kv_dtype == FD_DTYPE_BF16) {
+    if (head_dim == 128) return paged ? launch<128, __bf16, true>(p, stream) : launch<128, __bf16, false>(p, stream);
+    if (head_dim == 64) return paged ? launch<64, __bf16, true>(p, stream) : launch<64, __bf16, false>(p, stream);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int* out) {
+  const bool paged = layout == FD_LAYOUT_PAGED;
+  if (kv_dtype == FD_DTYPE_F16) {
+    if (head_dim == 128) return paged ? occupancy<128, _Float16, true>(out) : occupancy<128, _Float16, false>(out);
+    if (head_dim == 64) return paged ? occupancy<64, _Float16, true>(out) : occupancy<64, _Float16, false>(out);
+  } else if (kv_dtype == FD_DTYPE_BF16) {
+    if (head_dim == 128) return paged ? occupancy<128, __bf16, true>(out) : occupancy<128, __bf16, false>(out);
+    if (head_dim == 64) return paged ? occupancy<64, __bf16, true>(out) : occupancy<64, __bf16, false>(out);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace fd

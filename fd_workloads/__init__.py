@@ -46,6 +46,7 @@ class Workload:
     chunk_tokens: int = 0           # 0 = derived from num_splits
     ws_format: str = "uml"          # "uml" (u, m, l) or "olse" (o, lse)
     scale: float = 0.0              # 0 = 1/sqrt(D)
+    k_gain: float = 1.0             # K was drawn as k_gain * N(0, 1)
 
     @property
     def batch(self) -> int:
@@ -107,7 +108,7 @@ def contiguous(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int,
     sl = torch.as_tensor(seq_lens, dtype=torch.int32).to(device)
     assert sl.shape == (batch,) and int(sl.max()) <= capacity
     return Workload(name, q, k, v, sl, num_splits=num_splits, chunk_tokens=chunk_tokens,
-                    ws_format=ws_format)
+                    ws_format=ws_format, k_gain=k_gain)
 
 
 def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head_dim: int,
@@ -136,6 +137,17 @@ def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head
     v = _randn(gen, (num_pages, page_size, kv_heads, head_dim), dt, device)
     return Workload(name, q, k, v, sl.to(device), block_table=table.to(device),
                     page_size=page_size, num_splits=num_splits, chunk_tokens=chunk_tokens)
+
+
+def redraw_kv(w: Workload, seed: int) -> Workload:
+    """A copy of ``w`` with K and V drawn again (same shapes, dtype, device, gain
+    and lengths; q and block table shared): extra cache copies for a benchmark
+    that must not find one step's K/V in cache from the previous step."""
+    gen = torch.Generator(device=w.k.device)
+    gen.manual_seed(seed)
+    k = _randn(gen, tuple(w.k.shape), w.k.dtype, w.k.device, w.k_gain)
+    v = _randn(gen, tuple(w.v.shape), w.v.dtype, w.v.device)
+    return dataclasses.replace(w, k=k, v=v)
 
 
 def uniform_lengths(seed: int, batch: int, lo: int, hi: int) -> torch.Tensor:

@@ -1,0 +1,215 @@
+/*
+ * fd.h -- C ABI of the split-KV (Flash-Decoding) decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. For every sequence b and query head hq, one decode query
+ * row q[b, hq, :] attends over the first seq_lens[b] cached keys/values of KV
+ * head hkv = hq / g (g = Hq / Hkv):
+ *     s_i = scale * q . k_i,   O = sum_i softmax(s)_i v_i,   LSE = ln sum_i e^{s_i}
+ * ("Flash-Decoding: Split-KV Attention for Long-Context Decode", kanthi.in,
+ * §1 equation and §2 definition of the attention state). The KV sequence is cut
+ * into num_splits splits; fd_decode_split computes one attention state per
+ * split (§4 kernel 1; per-split (m, l, u) of the xuujii KB page "Decode 专项
+ * Attention" §04), and fd_merge combines them exactly by rescaling to the common
+ * maximum (kanthi.in §2 stable form; xuujii §04 rebase).
+ *
+ * Call sequence: fd_plan (host only, once per shape) -> fd_decode_split ->
+ * fd_merge, the last two on the caller's stream, back to back.
+ *
+ * Ownership and threading. The caller owns every buffer (q, K/V or pools,
+ * block table, seq_lens, workspace, output, LSE). The library allocates no
+ * device memory, keeps no state between calls (apart from a per-process cache
+ * of the device's CU count), launches asynchronously on the given stream and
+ * never synchronises. All entry points are thread-safe. Device pointers must
+ * stay valid until the launched work completes.
+ *
+ * Errors. Every entry point returns an fd_status. All validation runs on the
+ * host before any launch; on an error nothing is launched and no output is
+ * written. FD_ERR_HIP reports a failed launch (the HIP status is folded into
+ * the message of fd_last_hip_error()). No C++ exception crosses this ABI.
+ *
+ * Numerics. Accumulation, scores, running max/sum and the workspace are fp32
+ * whatever the cache dtype (kanthi.in §4 "FP32 everywhere it matters"); the
+ * output is fp32; LSE values are NATURAL logarithms (kanthi.in §8 asks that the
+ * base be stated). An empty split stores the neutral state (o = 0 / u = 0,
+ * m = LSE = -inf, l = 0) (kanthi.in §4); a row with seq_len 0 gets O = 0 and
+ * LSE = -inf. For a fixed plan, results are bitwise reproducible run to run.
+ */
+#ifndef FD_H_
+#define FD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FD_API __attribute__((visibility("default")))
+
+#define FD_VERSION_STRING "0.1.0"
+#define FD_PLAN_MAGIC 0x46445031u /* "FDP1" */
+
+typedef enum {
+  FD_OK = 0,
+  FD_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride, Hq % Hkv != 0, ... */
+  FD_ERR_UNSUPPORTED = 2,  /* head_dim, dtype or layout combination not built */
+  FD_ERR_ALIGNMENT = 3,    /* a pointer or row stride is not 16-byte aligned */
+  FD_ERR_WORKSPACE = 4,    /* workspace smaller than the plan requires */
+  FD_ERR_HIP = 5,          /* a HIP call or kernel launch failed */
+  FD_ERR_BAD_PLAN = 6      /* plan not produced by fd_plan, or modified since */
+} fd_status;
+
+typedef enum { FD_DTYPE_F32 = 0, FD_DTYPE_F16 = 1, FD_DTYPE_BF16 = 2 } fd_dtype;
+
+typedef enum {
+  /* K, V: [B, Hkv, T_cap, D] with element strides (b, h, t) and d contiguous
+   * (kanthi.in §4 wrapper and §9 decode contract). */
+  FD_LAYOUT_CONTIGUOUS = 0,
+  /* K, V pools: [num_pages, page_size, Hkv, D] with element strides
+   * (page, token, head) and d contiguous; block_table int32 [B, max_pages],
+   * token t of sequence b is row t % page_size of page block_table[b, t /
+   * page_size] (kanthi.in §7 paged-KV row and §9; the pool layout itself is
+   * this library's choice). */
+  FD_LAYOUT_PAGED = 1
+} fd_layout;
+
+typedef enum {
+  /* Per split: u = sum e^{s-m} v (unnormalised), m = max s, l = sum e^{s-m}
+   * (xuujii §04; tinyvolt "Write partial": the split kernel divides nothing). */
+  FD_WS_UML = 0,
+  /* Per split: o = u / l (normalised) and lse = m + ln l (kanthi.in §4 kernel 1
+   * workspace: fp32 partial output plus its LSE). */
+  FD_WS_OLSE = 1
+} fd_ws_format;
+
+typedef enum {
+  FD_KERNEL_AUTO = 0,  /* MFMA for 16-bit KV with 2 <= g <= 8, VALU otherwise */
+  FD_KERNEL_MFMA = 1,  /* packed-GQA tile on MFMA 16x16x32 (16-bit KV, g <= 8) */
+  FD_KERNEL_VALU = 2   /* one query head per lane row, DPP dot products */
+} fd_kernel;
+
+typedef enum {
+  /* Wave-efficiency rule of kanthi.in §6 on slots = CUs x resident
+   * workgroups per CU, restricted to split counts whose workspace traffic
+   * stays within overhead_budget of the KV bytes (§6 overhead check). */
+  FD_HEURISTIC_MI355X = 0,
+  /* The §6 rule exactly as printed: slots = 2 x CUs, block = 128 tokens, no
+   * traffic bound. Kept to reproduce the page's table. */
+  FD_HEURISTIC_FA2 = 1
+} fd_heuristic;
+
+/* Shape and layout of one decode step. All strides are in ELEMENTS. */
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t num_q_heads;    /* Hq >= 1 */
+  int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D in {64, 128} */
+  int32_t q_dtype;        /* fd_dtype; must equal kv_dtype */
+  int32_t kv_dtype;       /* fd_dtype */
+  int32_t layout;         /* fd_layout */
+  int32_t max_seq_len;    /* host-side upper bound of seq_lens[]; the plan's splits cover it */
+  int64_t q_stride_b;     /* q[b, h, d] at q + b*q_stride_b + h*q_stride_h + d */
+  int64_t q_stride_h;
+  /* FD_LAYOUT_CONTIGUOUS */
+  int64_t kv_stride_b;
+  int64_t kv_stride_h;
+  int64_t kv_stride_t;
+  int32_t kv_capacity;    /* T_cap: tokens allocated per (b, h); seq_lens are clamped to it */
+  /* FD_LAYOUT_PAGED */
+  int32_t page_size;      /* tokens per page: a power of two >= 16 */
+  int32_t num_pages;      /* pages in the pool; block-table entries are clamped to it */
+  int32_t max_pages_per_seq;  /* block_table row length used for addressing */
+  int64_t bt_stride_b;    /* block_table[b, p] at block_table + b*bt_stride_b + p */
+  int64_t pool_stride_page;
+  int64_t pool_stride_t;
+  int64_t pool_stride_h;
+  float scale;            /* score scale; 0 selects 1/sqrt(D) */
+  int32_t reserved0;
+} fd_problem;
+
+/* Planner options. Zero-initialise for the defaults. */
+typedef struct {
+  int32_t num_cus;            /* 0: ask the current device (hipGetDeviceProperties) */
+  int32_t wgs_per_cu;         /* 0: the chosen kernel's resident workgroups per CU */
+  int32_t force_splits;       /* > 0: use this many splits (0 = heuristic, FA2's num_splits=0) */
+  int32_t force_chunk_tokens; /* > 0: tokens per split (e.g. 1024); S = cdiv(max_seq_len, chunk) */
+  int32_t ws_format;          /* fd_ws_format */
+  int32_t kernel;             /* fd_kernel */
+  int32_t heuristic;          /* fd_heuristic */
+  int32_t max_splits;         /* 0: 128 */
+  float overhead_budget;      /* 0: 0.02 (workspace bytes <= 2% of KV bytes) */
+  int32_t reserved[7];
+} fd_plan_opts;
+
+/* A plan: caller-owned plain data, produced by fd_plan and read by the other
+ * calls. Do not modify; fd_decode_split/fd_merge re-validate it. */
+typedef struct {
+  uint32_t magic;             /* FD_PLAN_MAGIC */
+  int32_t num_splits;         /* S >= 1 */
+  int32_t chunk_tokens;       /* split s covers [s*chunk, min(s*chunk + chunk, seq_len)) */
+  int32_t kernel;             /* fd_kernel actually used (never AUTO) */
+  int32_t ws_format;          /* fd_ws_format */
+  int32_t group;              /* g = Hq / Hkv */
+  int32_t tile_tokens;        /* KV tokens one wave consumes per loop iteration */
+  int32_t waves_per_wg;       /* waves per split workgroup */
+  int32_t slots;              /* CUs x resident workgroups per CU used by the heuristic */
+  int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (S, Hkv, B) */
+  float scale;                /* resolved score scale */
+  int32_t reserved1;
+  int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
+  int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
+  fd_problem prob;            /* copy of the problem */
+  uint64_t checksum;          /* over the fields above */
+} fd_plan_t;
+
+/* Device pointers of one decode step. */
+typedef struct {
+  const void* q;              /* [B, Hq, D] (strided as in the problem) */
+  const void* k;              /* contiguous K or the K pool */
+  const void* v;              /* contiguous V or the V pool (same strides as K) */
+  const int32_t* seq_lens;    /* [B] int32; values are clamped to [0, capacity] */
+  const int32_t* block_table; /* paged only, else NULL */
+} fd_args;
+
+/* Choose the split count, chunk, kernel and workspace sizes for a problem
+ * (kanthi.in §6; xuujii §07 "choose a split plan for the current batch/head/
+ * length"). Host only; touches the device only when opts->num_cus == 0.
+ * opts may be NULL (all defaults). */
+FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* out);
+
+/* Split kernel: for every (b, kv head, split) one workgroup streams the split's
+ * K/V tokens, runs the fp32 online softmax for the g query heads of the group
+ * and writes their states to the workspace (kanthi.in §4 kernel 1; tinyvolt
+ * "fd_split"). ws_o: float [B, Hq, S, D]; ws_stats: see fd_plan_t. The
+ * workspace is fully overwritten (empty splits write the neutral state). */
+FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args,
+                           float* ws_o, size_t ws_o_bytes,
+                           float* ws_stats, size_t ws_stats_bytes, void* stream);
+
+/* Merge kernel: per (b, hq), O = sum_s w_s u_s / sum_s w_s l_s with
+ * w_s = e^{m_s - max_s m_s} (UML) or O = sum_s w_s o_s / sum_s w_s with
+ * w_s = e^{lse_s - max lse} (OLSE); LSE = max + ln(sum) (kanthi.in §2 stable
+ * form, §4 kernel 2; xuujii §04). Splits with m = -inf weigh 0.
+ * out: float [B, Hq, D] contiguous; lse: float [B, Hq] or NULL. */
+FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats,
+                    float* out, float* lse, void* stream);
+
+/* Human-readable text for an fd_status. Never NULL. */
+FD_API const char* fd_status_str(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+FD_API const char* fd_last_hip_error(void);
+
+/* Library version, FD_VERSION_STRING. */
+FD_API const char* fd_version(void);
+
+/* sizeof of the ABI structs, so bindings can check their mirrors:
+ * which = 0 fd_problem, 1 fd_plan_opts, 2 fd_plan_t, 3 fd_args; else 0. */
+FD_API size_t fd_struct_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H_ */

@@ -1,0 +1,220 @@
+"""Host-side tests of the C ABI (no GPU): symbols, struct layouts, planner and
+argument validation. Nothing here launches a kernel."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import decode_attention_fd_amd as fd
+from oracle import plan as OP
+from tests.conftest import ROOT, golden
+
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"FD_API\s+[\w\s\*]+?\b(fd_\w+)\s*\(", src)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fd.lib()
+    names = _declared_functions()
+    assert set(names) >= {"fd_plan", "fd_decode_split", "fd_merge", "fd_status_str", "fd_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert fd.version() == re.search(r'FD_VERSION_STRING "([^"]+)"', open(HEADER).read()).group(1)
+
+
+def test_struct_sizes_match_header():
+    L = fd.lib()
+    for i, cls in enumerate((fd.Problem, fd.PlanOpts, fd.Plan, fd.Args)):
+        assert L.fd_struct_size(i) == ctypes.sizeof(cls)
+    assert L.fd_struct_size(99) == 0
+
+
+def test_status_strings():
+    for s in range(7):
+        assert fd.status_str(s)
+    assert fd.status_str(12345) == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# Planner
+# ---------------------------------------------------------------------------
+
+def contiguous_problem(B=1, Hq=8, Hkv=8, D=128, L=1000, dtype=1, cap=None, **kw):
+    p = fd.Problem()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = B, Hq, Hkv, D
+    p.q_dtype = p.kv_dtype = dtype
+    p.layout = fd.LAYOUT_CONTIGUOUS
+    p.max_seq_len = L
+    cap = L if cap is None else cap
+    p.q_stride_h = D
+    p.q_stride_b = Hq * D
+    p.kv_stride_t = D
+    p.kv_stride_h = cap * D
+    p.kv_stride_b = Hkv * cap * D
+    p.kv_capacity = cap
+    for k_, v_ in kw.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def paged_problem(B=2, Hq=32, Hkv=8, D=128, L=1000, page=16, dtype=1, **kw):
+    p = fd.Problem()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = B, Hq, Hkv, D
+    p.q_dtype = p.kv_dtype = dtype
+    p.layout = fd.LAYOUT_PAGED
+    p.max_seq_len = L
+    p.q_stride_h = D
+    p.q_stride_b = Hq * D
+    p.page_size = page
+    p.max_pages_per_seq = -(-L // page)
+    p.num_pages = B * p.max_pages_per_seq
+    p.bt_stride_b = p.max_pages_per_seq
+    p.pool_stride_h = D
+    p.pool_stride_t = Hkv * D
+    p.pool_stride_page = page * Hkv * D
+    for k_, v_ in kw.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def test_fa2_heuristic_reproduces_page_table():
+    g = golden("split_table.json")
+    for row in g["rows"]:
+        prob = contiguous_problem(B=row["batch"], Hq=row["heads"], Hkv=row["heads"], L=row["context"])
+        plan = fd.fd_plan(prob, num_cus=g["sms"], wgs_per_cu=2, heuristic="fa2")
+        assert plan.num_splits == row["splits"], row
+        assert plan.grid_x * plan.grid_y * plan.grid_z == row["ctas"]
+        assert plan.slots == g["slots"]
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_mi355x_heuristic_matches_oracle_rule(kernel):
+    cus, wgs = 256, 2
+    budget = 0.02
+    for B in (1, 2, 4, 16, 64):
+        for Hkv, g in ((8, 8), (8, 4), (32, 1), (2, 2)):
+            if (kernel == "mfma" and g == 1) or (kernel == "valu" and g > 4):
+                continue
+            for L in (1, 100, 1000, 4096, 32768, 128000):
+                prob = contiguous_problem(B=B, Hq=Hkv * g, Hkv=Hkv, L=L)
+                plan = fd.fd_plan(prob, num_cus=cus, wgs_per_cu=wgs, kernel=kernel)
+                block = plan.tile_tokens * plan.waves_per_wg
+                s = OP.num_splits_traffic(B * Hkv, cus * wgs, math.ceil(L / block), 128, g, 128, 2, L, budget)
+                chunk = OP.chunk_for(L, s, block)
+                assert plan.chunk_tokens == chunk, (B, Hkv, g, L)
+                assert plan.num_splits == math.ceil(L / chunk), (B, Hkv, g, L)
+                assert plan.num_splits <= s
+
+
+def test_forced_splits_and_chunk():
+    p = fd.fd_plan(contiguous_problem(Hq=4, Hkv=4, D=64, L=1000, dtype=0), num_cus=256, force_splits=3)
+    assert (p.num_splits, p.chunk_tokens) == (3, 334)
+    p = fd.fd_plan(contiguous_problem(Hq=4, Hkv=4, D=64, L=1000, dtype=0), num_cus=256, force_splits=8)
+    assert (p.num_splits, p.chunk_tokens) == (8, 125)
+    p = fd.fd_plan(contiguous_problem(Hq=32, Hkv=32, L=65536, dtype=2), num_cus=256, force_chunk_tokens=1024,
+                   ws_format="olse")
+    assert (p.num_splits, p.chunk_tokens, p.ws_format) == (64, 1024, 1)
+    assert p.ws_stats_bytes == 32 * 64 * 4 and p.ws_o_bytes == 32 * 64 * 128 * 4
+    # paged: chunks are page- and tile-aligned
+    p = fd.fd_plan(paged_problem(L=1000), num_cus=256, force_splits=3)
+    assert p.chunk_tokens % 32 == 0 and p.num_splits * p.chunk_tokens >= 1000
+
+
+def test_kernel_choice():
+    assert fd.fd_plan(contiguous_problem(Hq=64, Hkv=8), num_cus=256).kernel == fd.KERNELS["mfma"]
+    assert fd.fd_plan(contiguous_problem(Hq=8, Hkv=8), num_cus=256).kernel == fd.KERNELS["valu"]
+    assert fd.fd_plan(contiguous_problem(Hq=16, Hkv=8, dtype=0), num_cus=256).kernel == fd.KERNELS["valu"]
+    assert fd.fd_plan(contiguous_problem(Hq=8, Hkv=8), num_cus=256, kernel="mfma").kernel == fd.KERNELS["mfma"]
+
+
+def _status(prob, **opts):
+    try:
+        fd.fd_plan(prob, num_cus=256, **opts)
+        return fd.FD_OK
+    except fd.FdError as e:
+        return e.status
+
+
+def test_problem_validation():
+    assert _status(contiguous_problem(Hq=12, Hkv=8)) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(D=96)) == fd.FD_ERR_UNSUPPORTED
+    assert _status(contiguous_problem(q_dtype=0)) == fd.FD_ERR_UNSUPPORTED
+    assert _status(contiguous_problem(kv_dtype=7, q_dtype=7)) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(L=1000, cap=999)) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(kv_stride_t=132)) == fd.FD_ERR_ALIGNMENT
+    assert _status(contiguous_problem(q_stride_h=129)) == fd.FD_ERR_ALIGNMENT
+    assert _status(contiguous_problem(batch=0)) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(layout=5)) == fd.FD_ERR_INVALID_ARG
+    assert _status(paged_problem(page=8)) == fd.FD_ERR_UNSUPPORTED
+    assert _status(paged_problem(page=24)) == fd.FD_ERR_UNSUPPORTED
+    assert _status(paged_problem(L=1000, max_pages_per_seq=10)) == fd.FD_ERR_INVALID_ARG
+    assert _status(paged_problem(), force_chunk_tokens=40) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(Hq=64, Hkv=8, dtype=0)) == fd.FD_ERR_UNSUPPORTED    # fp32, g = 8
+    assert _status(contiguous_problem(Hq=128, Hkv=8)) == fd.FD_ERR_UNSUPPORTED            # g = 16
+    assert _status(contiguous_problem(dtype=0), kernel="mfma") == fd.FD_ERR_UNSUPPORTED
+    assert _status(contiguous_problem(L=1000), force_chunk_tokens=100, force_splits=5) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(scale=float("nan"))) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(L=0)) == fd.FD_OK
+
+
+def test_plan_resolves_scale_and_workspace():
+    p = fd.fd_plan(contiguous_problem(B=2, Hq=16, Hkv=8, D=64, L=500), num_cus=256)
+    assert abs(p.scale - 1 / 8) < 1e-7
+    assert p.ws_o_bytes == 2 * 16 * p.num_splits * 64 * 4
+    assert p.ws_stats_bytes == 2 * 16 * p.num_splits * 2 * 4
+    p = fd.fd_plan(contiguous_problem(scale=0.3), num_cus=256)
+    assert abs(p.scale - 0.3) < 1e-7
+
+
+# ---------------------------------------------------------------------------
+# Decode/merge argument validation: every case fails before any HIP call.
+# ---------------------------------------------------------------------------
+
+def _split_status(plan, args, ws_o=4096, ws_o_bytes=1 << 40, ws_st=8192, ws_st_bytes=1 << 40):
+    return fd.lib().fd_decode_split(ctypes.byref(plan), ctypes.byref(args) if args is not None else None,
+                                    ws_o, ws_o_bytes, ws_st, ws_st_bytes, None)
+
+
+def test_decode_and_merge_validation_without_gpu():
+    plan = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8), num_cus=256)
+    good = fd.Args(0x10000, 0x20000, 0x30000, 0x40000, None)
+    assert _split_status(plan, None) == fd.FD_ERR_INVALID_ARG
+    assert _split_status(plan, fd.Args(0, 0x20000, 0x30000, 0x40000, None)) == fd.FD_ERR_INVALID_ARG
+    assert _split_status(plan, fd.Args(0x10008, 0x20000, 0x30000, 0x40000, None)) == fd.FD_ERR_ALIGNMENT
+    assert _split_status(plan, good, ws_o=4100) == fd.FD_ERR_ALIGNMENT
+    assert _split_status(plan, good, ws_o_bytes=plan.ws_o_bytes - 4) == fd.FD_ERR_WORKSPACE
+    assert _split_status(plan, good, ws_st_bytes=plan.ws_stats_bytes - 4) == fd.FD_ERR_WORKSPACE
+    bad = fd.Plan.from_buffer_copy(plan)
+    bad.num_splits += 1
+    assert _split_status(bad, good) == fd.FD_ERR_BAD_PLAN
+    bad = fd.Plan.from_buffer_copy(plan)
+    bad.magic = 0
+    assert _split_status(bad, good) == fd.FD_ERR_BAD_PLAN
+    L = fd.lib()
+    assert L.fd_merge(ctypes.byref(bad), 4096, 8192, 4096, None, None) == fd.FD_ERR_BAD_PLAN
+    assert L.fd_merge(ctypes.byref(plan), None, 8192, 4096, None, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_merge(ctypes.byref(plan), 4096, 8192, 4100, None, None) == fd.FD_ERR_ALIGNMENT
+    paged = fd.fd_plan(paged_problem(), num_cus=256)
+    assert _split_status(paged, good) == fd.FD_ERR_INVALID_ARG          # no block table
+
+
+def test_problem_for_tensors():
+    q = torch.zeros(2, 16, 128, dtype=torch.float16)
+    k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)
+    sl = torch.tensor([300, 5], dtype=torch.int32)
+    p = fd.problem_for(q, k, k, sl)
+    assert (p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len) == (2, 16, 4, 128, 300)
+    assert (p.kv_stride_b, p.kv_stride_h, p.kv_stride_t, p.kv_capacity) == (4 * 300 * 128, 300 * 128, 128, 300)
+    pool = torch.zeros(10, 16, 4, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 5, dtype=torch.int32)
+    p = fd.problem_for(q.to(torch.bfloat16), pool, pool, torch.tensor([70, 3], dtype=torch.int32), bt)
+    assert (p.layout, p.page_size, p.num_pages, p.max_pages_per_seq, p.pool_stride_t) == (1, 16, 10, 5, 512)
+    with pytest.raises(ValueError):
+        fd.problem_for(q, k, k[:, :, :200], sl)

@@ -1,0 +1,95 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (plan defaults unless the workload forces splits/chunks).
+Outputs are checked on sampled (sequence, head) pairs the oracle computes one
+by one; properties that hold at any size (finite, NaN-free, neutral empty
+splits) are checked everywhere."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fd_amd as fd
+import fd_workloads as W
+from oracle import attention as A
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _finite_everywhere(out, lse, seq_lens):
+    assert torch.all(torch.isfinite(out))
+    nonempty = seq_lens > 0
+    assert torch.all(torch.isfinite(lse[nonempty]))
+
+
+@pytest.mark.parametrize("splits", [3, 1, 2, 4, 5, 6, 7, 8])
+def test_tiny_mha_f32_config(splits):
+    w = W.tiny_mha_f32(num_splits=splits)
+    plan, out, lse, _, _ = H.run(w)
+    H.check_against_oracle(w, out, lse)
+
+
+def test_long_gqa_f16_128k():
+    w = W.long_gqa_f16()
+    plan, out, lse, _, _ = H.run(w)
+    H.say(f"long GQA plan: S={plan.num_splits} chunk={plan.chunk_tokens} slots={plan.slots}")
+    assert plan.kernel == fd.KERNELS["mfma"] and plan.num_splits > 1
+    _finite_everywhere(out, lse, w.seq_lens)
+    pairs = [(0, h) for h in (0, 7, 8, 21, 34, 47, 56, 63)]      # every KV group sampled
+    H.check_against_oracle(w, out, lse, pairs)
+
+
+def test_mha_bf16_fixed_chunks():
+    w = W.mha_bf16_chunked()
+    plan, out, lse, ws_o, ws_stats = H.run(w)
+    assert plan.num_splits == 64 and plan.chunk_tokens == 1024 and plan.ws_format == fd.WS_FORMATS["olse"]
+    _finite_everywhere(out, lse, w.seq_lens)
+    pairs = [(0, h) for h in (0, 5, 13, 31)]
+    H.check_against_oracle(w, out, lse, pairs)
+    # the (o, lse) workspace of one head against the oracle's split states
+    M, L, U = A.split_states(H.cache_of(w), 64, 1024, pairs=[(0, 5)])
+    o_s, lse_s = ws_o[0, 5].double().numpy(), ws_stats[0, 5, :, 0].double().numpy()
+    for s in range(64):
+        o_ref, l_ref = A.state_to_olse(M[0, 5, s], L[0, 5, s], U[0, 5, s])
+        assert np.abs(o_s[s] - o_ref).max() < 2e-3
+        assert abs(lse_s[s] - l_ref) < 1e-5 * max(1, abs(l_ref))
+
+
+def test_paged_ragged_f16():
+    w = W.paged_ragged_f16()
+    plan, out, lse, _, _ = H.run(w)
+    H.say(f"paged plan: S={plan.num_splits} chunk={plan.chunk_tokens}")
+    _finite_everywhere(out, lse, w.seq_lens)
+    pairs = H.sample_pairs(w.batch, w.num_q_heads, 24, seed=4)
+    H.check_against_oracle(w, out, lse, pairs)
+
+
+def test_edge_gqa_plan_splits():
+    w = W.edge_gqa_f16()
+    plan, out, lse, _, _ = H.run(w)
+    H.say(f"edge plan: S={plan.num_splits}")
+    assert plan.num_splits == 1                         # 512 work units fill the machine
+    H.check_against_oracle(w, out, lse)                 # every (b, hq)
+
+
+def test_edge_gqa_forced_masked_splits():
+    w = W.edge_gqa_f16(forced_splits=8)
+    plan, out, lse, ws_o, ws_stats = H.run(w)
+    assert plan.num_splits == 8 and plan.chunk_tokens == 256
+    H.check_against_oracle(w, out, lse)
+    o_s, lse_s, m_s, l_s = H.split_states_of(plan, ws_o, ws_stats)
+    n_masked = 0
+    for b, L in enumerate(w.seq_lens.tolist()):
+        for s in range(8):
+            if s * 256 >= L:
+                n_masked += 1
+                assert np.all(ws_o[b, :, s].numpy() == 0)
+                assert np.all(np.isneginf(m_s[b, :, s])) and np.all(l_s[b, :, s] == 0)
+    assert n_masked > 0
+    # one-token splits exist (lengths chunk*k + 1) and match the oracle's split state
+    rows = [b for b, L in enumerate(w.seq_lens.tolist()) if L % 256 == 1 and L > 1]
+    assert rows
+    b = rows[0]
+    s = w.seq_lens[b].item() // 256
+    M, Lw, U = A.split_states(H.cache_of(w), 8, 256, pairs=[(b, 0)])
+    assert abs(m_s[b, 0, s] - M[b, 0, s]) < 1e-5 * max(1, abs(M[b, 0, s]))
+    assert abs(l_s[b, 0, s] - 1.0) < 1e-6

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP split + merge path (through the C ABI) against the
+float64 oracle, element by element. Needs an MI355X and the built libfd.so."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fd_amd as fd
+import fd_workloads as W
+from oracle import attention as A
+from tests import gpu_helpers as H
+from tests.conftest import golden
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# Tiny MHA, fp32 (VALU path): every split count, both workspace forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("q_gain", [1.0, 40.0])
+def test_tiny_mha_f32_every_split_count(splits, q_gain):
+    w = W.tiny_mha_f32(num_splits=splits, q_gain=q_gain)
+    plan, out, lse, _, _ = H.run(w)
+    assert plan.num_splits == splits and plan.kernel == fd.KERNELS["valu"]
+    st = H.check_against_oracle(w, out, lse)
+    assert st["max_abs"] <= 1e-4          # fp32 cache: far inside the 2e-3 bar
+
+
+@pytest.mark.parametrize("fmt", ["uml", "olse"])
+def test_tiny_partial_states_match_oracle_splits(fmt):
+    w = W.tiny_mha_f32(num_splits=3)
+    plan, out, lse, ws_o, ws_stats = H.run(w, ws_format=fmt)
+    o_s, lse_s, m_s, l_s = H.split_states_of(plan, ws_o, ws_stats)
+    M, L, U = A.split_states(H.cache_of(w), plan.num_splits, plan.chunk_tokens)
+    for s in range(plan.num_splits):
+        for h in range(w.num_q_heads):
+            o_ref, lse_ref = A.state_to_olse(M[0, h, s], L[0, h, s], U[0, h, s])
+            assert np.abs(o_s[0, h, s] - o_ref).max() < 1e-5
+            assert abs(lse_s[0, h, s] - lse_ref) < 1e-5 * max(1, abs(lse_ref))
+            if fmt == "uml":           # m is the split's largest score, l its sum of e^(s - m)
+                assert abs(m_s[0, h, s] - M[0, h, s]) < 1e-5 * max(1, abs(M[0, h, s]))
+                assert abs(l_s[0, h, s] - L[0, h, s]) < 1e-5 * L[0, h, s]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("q_gain", [1.0, 40.0])
+def test_ragged_batch_with_empty_splits(splits, q_gain):
+    w = W.ragged_mha_f32(num_splits=splits, q_gain=q_gain)
+    plan, out, lse, ws_o, ws_stats = H.run(w)
+    H.check_against_oracle(w, out, lse)
+    o_s, lse_s, m_s, l_s = H.split_states_of(plan, ws_o, ws_stats)
+    # with 8 splits of 125 tokens the 37-token row has 7 empty splits: neutral states, exactly
+    for b, L in enumerate(w.seq_lens.tolist()):
+        for s in range(plan.num_splits):
+            if s * plan.chunk_tokens >= L:
+                assert np.all(ws_o[b, :, s].numpy() == 0)
+                assert np.all(np.isneginf(m_s[b, :, s])) and np.all(l_s[b, :, s] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Packed GQA on MFMA, fp16 / bf16, several tiles and a ragged tail
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_gqa_mfma_small(dtype, g, D):
+    w = W.contiguous(f"gqa_g{g}_D{D}_{dtype}", seed=10 + g, batch=2, q_heads=4 * g, kv_heads=4, head_dim=D,
+                     capacity=3001, seq_lens=[3001, 1234], dtype=dtype)
+    for splits in (0, 1, 3, 7):
+        plan, out, lse, _, _ = H.run(w, force_splits=splits) if splits else H.run(w)
+        assert plan.kernel == fd.KERNELS["mfma"]
+        H.check_against_oracle(w, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_valu_small_groups(dtype, g):
+    w = W.contiguous(f"valu_g{g}_{dtype}", seed=20 + g, batch=2, q_heads=2 * g, kv_heads=2, head_dim=128,
+                     capacity=2500, seq_lens=[2500, 77], dtype=dtype)
+    for splits in (1, 4):
+        plan, out, lse, _, _ = H.run(w, force_splits=splits, kernel="valu")
+        H.check_against_oracle(w, out, lse)
+
+
+def test_mfma_forced_for_mha():
+    w = W.contiguous("mha_mfma_bf16", seed=31, batch=2, q_heads=4, kv_heads=4, head_dim=128, capacity=1500,
+                     seq_lens=[1500, 700], dtype="bf16")
+    plan, out, lse, _, _ = H.run(w, kernel="mfma", force_splits=5)
+    assert plan.kernel == fd.KERNELS["mfma"]
+    H.check_against_oracle(w, out, lse)
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513])
+def test_sequence_edges(L):
+    """seq_len at 1, tile - 1, tile, tile + 1 and chunk*k +- 1 (chunk 128)."""
+    w = W.contiguous(f"edge_L{L}", seed=40, batch=1, q_heads=16, kv_heads=2, head_dim=128, capacity=600,
+                     seq_lens=[L], dtype="f16")
+    plan, out, lse, _, _ = H.run(w, force_chunk_tokens=128, force_splits=5)
+    H.check_against_oracle(w, out, lse)
+    w2 = W.contiguous(f"edge_valu_L{L}", seed=41, batch=1, q_heads=2, kv_heads=2, head_dim=64, capacity=600,
+                      seq_lens=[L], dtype="bf16")
+    plan, out, lse, _, _ = H.run(w2, force_chunk_tokens=128, force_splits=5)
+    H.check_against_oracle(w2, out, lse)
+
+
+def test_zero_length_rows():
+    w = W.contiguous("zero_rows", seed=42, batch=3, q_heads=8, kv_heads=2, head_dim=128, capacity=300,
+                     seq_lens=[0, 300, 0], dtype="f16")
+    plan, out, lse, _, _ = H.run(w, force_splits=2)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[2]))
+    H.check_against_oracle(w, out, lse)
+
+
+# ---------------------------------------------------------------------------
+# Paged layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("page", [16, 32, 64])
+@pytest.mark.parametrize("g", [1, 4])
+def test_paged_small(page, g):
+    lens = [1000, 17, 333, 16]
+    w = W.paged(f"paged_p{page}_g{g}", seed=50 + page, batch=4, q_heads=4 * g, kv_heads=4, head_dim=128,
+                seq_lens=lens, page_size=page, dtype="f16", extra_pages=3)
+    for splits in (1, 3):
+        plan, out, lse, _, _ = H.run(w, force_splits=splits)
+        H.check_against_oracle(w, out, lse)
+
+
+# ---------------------------------------------------------------------------
+# LSE checks: base and scale (merge two halves outside the library)
+# ---------------------------------------------------------------------------
+
+def test_external_merge_of_two_halves():
+    w = W.contiguous("halves", seed=60, batch=1, q_heads=16, kv_heads=2, head_dim=128, capacity=4000,
+                     seq_lens=[4000], dtype="f16", q_gain=3.0)
+    _, out, lse, _, _ = H.run(w)
+    parts = []
+    for lo, hi in ((0, 1700), (1700, 4000)):
+        wh = W.Workload("half", w.q, w.k[:, :, lo:hi].contiguous(), w.v[:, :, lo:hi].contiguous(),
+                        torch.tensor([hi - lo], dtype=torch.int32))
+        _, o_h, l_h, _, _ = H.run(wh)
+        parts.append((o_h.double().numpy(), l_h.double().numpy()))
+    O, LSE = A.decode_attention(H.cache_of(w))
+    for h in range(16):
+        om, lm = A.merge_olse([(p[0][0, h], p[1][0, h]) for p in parts])
+        assert np.abs(om - O[0, h]).max() < 2e-3
+        assert abs(lm - LSE[0, h]) < 1e-5 * max(1, abs(LSE[0, h]))
+        assert abs(lm - lse[0, h].item()) < 1e-5 * max(1, abs(LSE[0, h]))
+
+
+# ---------------------------------------------------------------------------
+# Merge kernel alone: the merge-trap states of the kanthi.in chapter §3
+# ---------------------------------------------------------------------------
+
+def test_merge_trap_states_through_fd_merge():
+    g = golden("merge_trap.json")
+    prob = fd.Problem()
+    prob.batch, prob.num_q_heads, prob.num_kv_heads, prob.head_dim = 1, 1, 1, 64
+    prob.q_dtype = prob.kv_dtype = 1
+    prob.max_seq_len = 3
+    prob.q_stride_h = prob.q_stride_b = 64
+    prob.kv_stride_t, prob.kv_stride_h, prob.kv_stride_b, prob.kv_capacity = 64, 192, 192, 3
+    plan = fd.fd_plan(prob, num_cus=256, force_splits=3, force_chunk_tokens=1, ws_format="olse")
+    ws_o = torch.zeros(1, 1, 3, 64, dtype=torch.float32)
+    ws_o[0, 0, :, :2] = torch.tensor(g["o_f32"])
+    ws_st = torch.tensor(g["lse_f32"], dtype=torch.float32).reshape(1, 1, 3, 1)
+    out = torch.empty(1, 1, 64, device="cuda")
+    lse = torch.empty(1, 1, device="cuda")
+    fd.fd_merge(plan, ws_o.cuda(), ws_st.cuda(), out, lse)
+    torch.cuda.synchronize()
+    pr = g["printed"]
+    np.testing.assert_allclose(out[0, 0, :2].cpu().numpy(), pr["stable_merge"], rtol=0, atol=1e-6)
+    assert torch.all(out[0, 0, 2:] == 0)
+    assert abs(lse.item() - pr["merged_lse"]) < 1e-4
+    # same states in the (u, m, l) form: u = o, m = lse, l = 1
+    plan_u = fd.fd_plan(prob, num_cus=256, force_splits=3, force_chunk_tokens=1, ws_format="uml")
+    ws_su = torch.stack([ws_st[..., 0], torch.ones_like(ws_st[..., 0])], -1)
+    fd.fd_merge(plan_u, ws_o.cuda(), ws_su.cuda(), out, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out[0, 0, :2].cpu().numpy(), pr["stable_merge"], rtol=0, atol=1e-6)
+
+
+def test_merge_all_empty_and_worked_example():
+    # worked example of the xuujii page as two (m, l, u) states with D = 64 (value in dim 0)
+    ex = golden("worked_example.json")
+    prob = fd.Problem()
+    prob.batch, prob.num_q_heads, prob.num_kv_heads, prob.head_dim = 2, 1, 1, 64
+    prob.q_dtype = prob.kv_dtype = 1
+    prob.max_seq_len = 4
+    prob.q_stride_h, prob.q_stride_b = 64, 64
+    prob.kv_stride_t, prob.kv_stride_h, prob.kv_stride_b, prob.kv_capacity = 64, 256, 256, 4
+    plan = fd.fd_plan(prob, num_cus=256, force_splits=2, force_chunk_tokens=2)
+    ws_o = torch.zeros(2, 1, 2, 64)
+    ws_st = torch.zeros(2, 1, 2, 2)
+    for s, blk in enumerate(ex["blocks"]):
+        ws_o[0, 0, s, 0] = blk["u"]
+        ws_st[0, 0, s] = torch.tensor([math.log(blk["m_log_of"]), blk["l"]])
+    ws_st[1, 0, :, 0] = -math.inf         # row 1: every split empty
+    out = torch.empty(2, 1, 64, device="cuda")
+    lse = torch.empty(2, 1, device="cuda")
+    fd.fd_merge(plan, ws_o.cuda(), ws_st.cuda(), out, lse)
+    torch.cuda.synchronize()
+    assert abs(out[0, 0, 0].item() - ex["output"]) < 1e-6
+    assert abs(lse[0, 0].item() - math.log(10.0)) < 1e-6
+    assert torch.all(out[1] == 0) and math.isinf(lse[1, 0].item()) and lse[1, 0].item() < 0
+
+
+# ---------------------------------------------------------------------------
+# Determinism and streams
+# ---------------------------------------------------------------------------
+
+def test_bitwise_deterministic_for_fixed_plan():
+    w = W.contiguous("det", seed=70, batch=2, q_heads=32, kv_heads=4, head_dim=128, capacity=5000,
+                     seq_lens=[5000, 4321], dtype="f16")
+    a = H.run(w, force_splits=6)
+    b = H.run(w, force_splits=6)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
+
+
+def test_runs_on_a_side_stream():
+    w = W.contiguous("stream", seed=71, batch=1, q_heads=8, kv_heads=1, head_dim=128, capacity=2000,
+                     seq_lens=[2000], dtype="bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan, out, lse, _, _ = H.run(w, stream=s)
+    H.check_against_oracle(w, out, lse)
+
+
+def test_occupancy_table_matches_device():
+    """The built-in resident-workgroup table the planner uses without a device
+    equals what the device reports for the same kernels."""
+    props = torch.cuda.get_device_properties(0)
+    cases = [(64, 8, 128, torch.float16, None), (32, 8, 64, torch.bfloat16, None), (32, 32, 128, torch.bfloat16, None),
+             (4, 4, 64, torch.float32, None), (32, 8, 128, torch.float16, 16), (8, 4, 128, torch.float16, None)]
+    for hq, hkv, d, dt, page in cases:
+        q = torch.zeros(1, hq, d, dtype=dt, device="cuda")
+        sl = torch.tensor([100], dtype=torch.int32, device="cuda")
+        if page:
+            k = torch.zeros(8, page, hkv, d, dtype=dt, device="cuda")
+            bt = torch.zeros(1, 8, dtype=torch.int32, device="cuda")
+        else:
+            k = torch.zeros(1, hkv, 100, d, dtype=dt, device="cuda")
+            bt = None
+        prob = fd.problem_for(q, k, k, sl, bt)
+        dev_plan = fd.fd_plan(prob)                                   # num_cus = 0: ask the device
+        host_plan = fd.fd_plan(prob, num_cus=props.multi_processor_count)
+        H.say(f"{hq}/{hkv} D{d} {dt} page={page}: CUs {props.multi_processor_count} device slots "
+              f"{dev_plan.slots} table slots {host_plan.slots}")
+        assert dev_plan.slots == host_plan.slots
