@@ -11,10 +11,11 @@
 // at the end with the exact rescaled merge (§2 stable form).
 //
 // Per wave tile of 32 tokens:
-//   * K and V rows are fetched with fully coalesced 16-byte loads (a wave
-//     instruction reads whole rows; the address is one scalar base per
-//     instruction plus a constant lane offset) into registers, one tile ahead
-//     of use, and written to the wave's own LDS slice. Rows are padded by 16
+//   * K and V rows are fetched with fully coalesced 16-byte nontemporal loads
+//     (a wave instruction reads whole rows; the address is one scalar base per
+//     instruction plus a constant lane offset; every byte is read once, so the
+//     loads are marked streaming) into registers, two tiles ahead of use, and
+//     written to the wave's own LDS slice. Rows are padded by 16
 //     bytes so the 16 rows one MFMA operand read touches fall in distinct bank
 //     groups, while every LDS access is one base register plus an immediate.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 tokens x 32 dims of
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
   const int col = lane & 15;     // MFMA column = query column
   const int grp = lane >> 4;     // 16-lane group
@@ -154,10 +155,9 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
     return pid;
   };
 
-  u32x4 kr[G::NI], vr[G::NI];
-  // Loads of the tile starting at t0. Instruction i reads rows t0 + i*RPI + [0, RPI).
-  // Rows past `end` (tail tile only) re-read row end-1.
-  auto issue = [&](int t0, int pids) {
+  // Loads of the tile starting at t0 into (kr, vr). Instruction i reads rows
+  // t0 + i*RPI + [0, RPI); rows past `end` (tail tile only) re-read row end-1.
+  auto issue = [&](u32x4 (&kr)[G::NI], u32x4 (&vr)[G::NI], int t0, int pids) {
     const bool full = t0 + TT <= end;               // wave-uniform
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
@@ -176,13 +176,21 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
         const int tc = t < end - 1 ? t : end - 1;
         loff = (uint32_t)((tc - tu) * row_stride) + lchunk * 16;
       }
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + ubase + loff);
-      vr[i] = *reinterpret_cast<const u32x4*>(vbase + ubase + loff);
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + ubase + loff));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + ubase + loff));
     }
   };
 
   unsigned char* ldsK = lds[wave][0];
   unsigned char* ldsV = lds[wave][1];
+  auto store = [&](const u32x4 (&kr)[G::NI], const u32x4 (&vr)[G::NI]) {
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+      const int off = (i * G::RPI + lrow) * G::ROWP + lchunk * 16;
+      *reinterpret_cast<u32x4*>(ldsK + off) = kr[i];
+      *reinterpret_cast<u32x4*>(ldsV + off) = vr[i];
+    }
+  };
 
   f32x4 oacc[G::NDB];
 #pragma unroll
@@ -191,30 +199,8 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   float l_run = 0.f;         // this lane's share of the running sum
   const float c2 = p.scale_log2;
 
-  int tile = wave;
-  int pid_cur = 0, pid_next = 0;
-  if (PAGED) {
-    if (tile < ntiles) pid_cur = page_ids(start + tile * TT);
-    if (tile + NW < ntiles) pid_next = page_ids(start + (tile + NW) * TT);
-  }
-  if (tile < ntiles) issue(start + tile * TT, pid_cur);
-
-  for (; tile < ntiles; tile += NW) {
-    const int t0 = start + tile * TT;
-    // registers -> padded LDS tile
-#pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-      const int off = (i * G::RPI + lrow) * G::ROWP + lchunk * 16;
-      *reinterpret_cast<u32x4*>(ldsK + off) = kr[i];
-      *reinterpret_cast<u32x4*>(ldsV + off) = vr[i];
-    }
-    // next tile's loads go out before this tile's math
-    const int nt = tile + NW;
-    if (nt < ntiles) {
-      issue(start + nt * TT, pid_next);
-      if (PAGED && nt + NW < ntiles) pid_next = page_ids(start + (nt + NW) * TT);
-    }
-
+  // One tile from the wave's LDS slice into the running state.
+  auto compute = [&](int t0) {
     // ---- S^T = K Q^T for tokens [0,16) and [16,32)
     f32x4 sacc[2];
 #pragma unroll
@@ -284,6 +270,40 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) a[jj] = pick_half(w[2 * jj][e >> 1], w[2 * jj + 1][e >> 1], e);
       oacc[e] = Mma<T>::run(__builtin_bit_cast(V8, a), pb, oacc[e]);
+    }
+  };
+
+  // Two register buffers: tiles t and t + NW are in flight while tile t - NW is
+  // consumed from LDS. Tile indices past the split are clamped to its last tile
+  // (a reload that hits in cache), so every load is unconditional.
+  const int last = ntiles - 1;
+  auto tstart = [&](int tile) { return start + (tile < last ? tile : last) * TT; };
+  if (ntiles > 0) {
+    u32x4 ka[G::NI], va[G::NI], kb2[G::NI], vb2[G::NI];
+    int tile = wave;
+    int pid_a = 0, pid_b = 0;
+    if (PAGED) {
+      pid_a = page_ids(tstart(tile));
+      pid_b = page_ids(tstart(tile + NW));
+    }
+    issue(ka, va, tstart(tile), pid_a);
+    issue(kb2, vb2, tstart(tile + NW), pid_b);
+    if (PAGED) {
+      pid_a = page_ids(tstart(tile + 2 * NW));
+      pid_b = page_ids(tstart(tile + 3 * NW));
+    }
+    // One exit at the bottom: the wait-count analysis then sees the same load
+    // order (A older than B) on entry and on the back edge.
+    const int my_tiles = (ntiles - wave + NW - 1) / NW;     // > 0 only if wave < ntiles
+    for (int it = 0; it < (my_tiles + 1) / 2; ++it, tile += 2 * NW) {
+      store(ka, va);
+      issue(ka, va, tstart(tile + 2 * NW), pid_a);
+      if (PAGED) pid_a = page_ids(tstart(tile + 4 * NW));
+      compute(start + tile * TT);
+      store(kb2, vb2);
+      issue(kb2, vb2, tstart(tile + 3 * NW), pid_b);
+      if (PAGED) pid_b = page_ids(tstart(tile + 5 * NW));
+      if (tile + NW < ntiles) compute(start + (tile + NW) * TT);
     }
   }
 

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
   const int rg = lane / LPR;     // row group
   const int li = lane % LPR;     // lane inside the row
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t off = offset(t0, u, pid_cur);
-      kb[u] = *reinterpret_cast<const u32x4*>(kbase + off);
-      vb[u] = *reinterpret_cast<const u32x4*>(vbase + off);
+      kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+      vb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
     }
   }
 
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
       for (int h = 0; h < G; ++h) x[h][u] = Elt<T>::dot(q[h], kb[u]);
     if (nt < ntiles) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) kb[u] = *reinterpret_cast<const u32x4*>(kbase + offset(tn0, u, pid_next));
+      for (int u = 0; u < U; ++u) kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + offset(tn0, u, pid_next)));
     }
     const bool tail = t0 + TT > end;
 #pragma unroll
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
       }
     if (nt < ntiles) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) vb[u] = *reinterpret_cast<const u32x4*>(vbase + offset(tn0, u, pid_next));
+      for (int u = 0; u < U; ++u) vb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + offset(tn0, u, pid_next)));
       if (PAGED && nt + NW < ntiles) pid_next = page_ids(start + (nt + NW) * TT);
     }
   }
