@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = planner)")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate (0 = enough for 2x the MALL)")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
+    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+                    help="fused: one launch (last workgroup per group merges); split: split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -154,6 +156,7 @@ def main():
     plan = fd.fd_plan(prob, **opts)
     plan_us = (time.perf_counter() - t0) * 1e6
     ws_o, ws_stats = fd.workspace(plan, dev)
+    ctr = fd.counters(plan, dev)
     out = torch.empty(w0.batch, w0.num_q_heads, w0.head_dim, dtype=torch.float32, device=dev)
     lse = torch.empty(w0.batch, w0.num_q_heads, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -162,10 +165,15 @@ def main():
         w = ws[i % copies]
         if evs is not None:
             evs[0].record(stream)
-        fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
-        if evs is not None:
-            evs[1].record(stream)
-        fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+        if args.path == "fused":
+            fd.fd_decode_fused(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, ctr, out, lse, w.block_table, stream)
+            if evs is not None:
+                evs[1].record(stream)
+        else:
+            fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
+            if evs is not None:
+                evs[1].record(stream)
+            fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
         if evs is not None:
             evs[2].record(stream)
 
@@ -216,7 +224,7 @@ def main():
             "kv_bytes_allocated": alloc, "kv_copies": copies, "layout": "paged" if w0.paged else "contiguous",
             "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
             "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
-            "slots": plan.slots, "plan_us": round(plan_us, 1),
+            "slots": plan.slots, "plan_us": round(plan_us, 1), "path": args.path,
         },
         "split_kernel_us": round(split_us, 2),
         "merge_kernel_us": round(merge_us, 2),

@@ -63,7 +63,7 @@ class Plan(ctypes.Structure):
         ("tile_tokens", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("slots", ctypes.c_int32),
         ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
         ("scale", ctypes.c_float), ("reserved1", ctypes.c_int32),
-        ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64),
+        ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64), ("ws_counter_bytes", ctypes.c_int64),
         ("prob", Problem), ("checksum", ctypes.c_uint64),
     ]
 
@@ -97,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.fd_decode_split.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.fd_decode_split.restype = ctypes.c_int
+        L.fd_decode_fused.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.fd_decode_fused.restype = ctypes.c_int
         L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge.restype = ctypes.c_int
@@ -213,6 +217,25 @@ def fd_decode_split(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, block_table=N
     _check(st, "fd_decode_split")
 
 
+def counters(plan: Plan, device) -> torch.Tensor:
+    """Zeroed arrival counters for fd_decode_fused (uint32 [B * Hkv]; kept zero by every call)."""
+    return torch.zeros(plan.ws_counter_bytes // 4, dtype=torch.int32, device=device)
+
+
+def fd_decode_fused(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, ctr, out, lse=None, block_table=None,
+                    stream=None) -> None:
+    """Split kernel with the merge fused in: writes out (and lse) in one launch."""
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor")
+    a = Args(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_table))
+    st = lib().fd_decode_fused(ctypes.byref(plan), ctypes.byref(a), _ptr(ws_o), ws_o.numel() * ws_o.element_size(),
+                               _ptr(ws_stats), ws_stats.numel() * ws_stats.element_size(), _ptr(ctr),
+                               ctr.numel() * ctr.element_size(), _ptr(out), _ptr(lse), _stream_handle(stream))
+    _check(st, "fd_decode_fused")
+
+
 def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:
     """Launch the merge kernel: out [B,Hq,D] fp32 (contiguous), lse [B,Hq] fp32 or None."""
     if out.dtype != torch.float32 or not out.is_contiguous():
@@ -225,12 +248,17 @@ def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:
 
 
 def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,
-                 return_lse: bool = True, stream=None, **plan_options):
-    """Plan, split and merge in one call; returns (out, lse) fp32 (lse None if not asked)."""
+                 return_lse: bool = True, fused: bool = False, stream=None, **plan_options):
+    """Plan, split and merge (two launches, or one with ``fused=True``); returns
+    (out, lse) fp32 (lse None if not asked)."""
     plan = fd_plan(problem_for(q, k, v, seq_lens, block_table, max_seq_len, scale), **plan_options)
     ws_o, ws_stats = workspace(plan, q.device)
     out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device) if return_lse else None
-    fd_decode_split(plan, q, k, v, seq_lens, ws_o, ws_stats, block_table, stream)
-    fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+    if fused:
+        fd_decode_fused(plan, q, k, v, seq_lens, ws_o, ws_stats, counters(plan, q.device), out, lse, block_table,
+                        stream)
+    else:
+        fd_decode_split(plan, q, k, v, seq_lens, ws_o, ws_stats, block_table, stream)
+        fd_merge(plan, ws_o, ws_stats, out, lse, stream)
     return out, lse

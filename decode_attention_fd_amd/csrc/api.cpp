@@ -117,6 +117,9 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   const int kernel = choose_kernel(prob, o.kernel);
   if (kernel < 0) return -kernel;
   const int gtpl = valu_group_template(prob->num_q_heads / prob->num_kv_heads);
+  // Resident split workgroups per CU: the device's answer when we query it,
+  // else the table generated from the compiler's resource usage.
+  int resident = 0;
   if (o.num_cus == 0) {
     int dev = 0, n = 0;
     int err = (int)hipGetDevice(&dev);
@@ -124,21 +127,24 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
     err = (int)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (err) return hip_fail(err, "hipDeviceGetAttribute");
     o.num_cus = n;
-    if (o.wgs_per_cu == 0) {
-      int occ = 0;
-      err = occupancy_split(kernel, prob->head_dim, prob->kv_dtype, prob->layout, gtpl, &occ);
-      if (err) return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-      o.wgs_per_cu = occ > 0 ? occ : 1;
-    }
+    err = occupancy_split(kernel, prob->head_dim, prob->kv_dtype, prob->layout, gtpl, &resident);
+    if (err) return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
-  if (o.wgs_per_cu == 0)
-    o.wgs_per_cu = default_wgs_per_cu(kernel, prob->head_dim, prob->kv_dtype, gtpl, prob->layout);
+  if (resident <= 0) resident = default_wgs_per_cu(kernel, prob->head_dim, prob->kv_dtype, gtpl, prob->layout);
+  // Workgroups per CU in one wave of the MI355X split rule: 1 by default (one
+  // streaming split workgroup per CU saturates its share of HBM; measured by
+  // split-count sweeps), never more than can be resident.
+  if (o.wgs_per_cu == 0) o.wgs_per_cu = 1;
+  if (o.wgs_per_cu > resident) o.wgs_per_cu = resident;
   o.kernel = kernel;
   return plan_core(prob, &o, out);
 }
 
-FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes,
-                           float* ws_stats, size_t ws_stats_bytes, void* stream) {
+namespace {
+
+// Validation and parameter setup shared by fd_decode_split and fd_decode_fused.
+int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes, float* ws_stats,
+                 size_t ws_stats_bytes, SplitParams* out) {
   int st = check_plan(plan);
   if (st != FD_OK) return st;
   if (!args || !args->q || !args->k || !args->v || !args->seq_lens || !ws_o || !ws_stats)
@@ -152,7 +158,7 @@ FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws
   if (ws_o_bytes < (size_t)plan->ws_o_bytes || ws_stats_bytes < (size_t)plan->ws_stats_bytes)
     return FD_ERR_WORKSPACE;
 
-  SplitParams p;
+  SplitParams& p = *out;
   memset(&p, 0, sizeof(p));
   p.q = args->q;
   p.k = args->k;
@@ -183,12 +189,16 @@ FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws
   } else {
     p.cap_tokens = pr.kv_capacity;
   }
-  // Splits past S*chunk are never launched: clamp there as well.
+  // Tokens past S*chunk belong to no split: clamp there as well.
   const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;
   if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
   p.ws_format = plan->ws_format;
   p.scale_log2 = (float)((double)plan->scale * 1.4426950408889634);
+  return FD_OK;
+}
 
+int launch_split(const fd_plan_t* plan, const SplitParams& p, void* stream) {
+  const fd_problem& pr = plan->prob;
   int err;
   if (plan->kernel == FD_KERNEL_MFMA)
     err = launch_split_mfma(p, pr.head_dim, pr.kv_dtype, pr.layout, stream);
@@ -196,6 +206,32 @@ FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws
     err = launch_split_valu(p, pr.head_dim, pr.kv_dtype, pr.layout, valu_group_template(plan->group), stream);
   if (err) return hip_fail(err, "split kernel launch");
   return FD_OK;
+}
+
+}  // namespace
+
+FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes,
+                           float* ws_stats, size_t ws_stats_bytes, void* stream) {
+  SplitParams p;
+  int st = split_params(plan, args, ws_o, ws_o_bytes, ws_stats, ws_stats_bytes, &p);
+  if (st != FD_OK) return st;
+  return launch_split(plan, p, stream);
+}
+
+FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes,
+                           float* ws_stats, size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes,
+                           float* out, float* lse, void* stream) {
+  SplitParams p;
+  int st = split_params(plan, args, ws_o, ws_o_bytes, ws_stats, ws_stats_bytes, &p);
+  if (st != FD_OK) return st;
+  if (!counters || !out) return FD_ERR_INVALID_ARG;
+  if (!aligned(counters, 4) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return FD_ERR_ALIGNMENT;
+  if (counters_bytes < (size_t)plan->ws_counter_bytes) return FD_ERR_WORKSPACE;
+  p.fused = 1;
+  p.counters = counters;
+  p.out = out;
+  p.lse = lse;
+  return launch_split(plan, p, stream);
 }
 
 FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats, float* out, float* lse,

@@ -28,6 +28,11 @@ struct SplitParams {
   int32_t page_log2, num_pages;
   int32_t ws_format;
   float scale_log2;                     // scale * log2(e): scores go straight to base 2
+  // fused merge (0 = write split states only)
+  int32_t fused;
+  uint32_t* counters;                   // [B * Hkv], zero on entry, zero on exit
+  float* out;                           // [B, Hq, D]
+  float* lse;                           // [B, Hq] or null
 };
 
 struct MergeParams {

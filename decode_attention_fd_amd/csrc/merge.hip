@@ -6,27 +6,19 @@
 //         LSE = M + ln(sum w_s l_s)
 //   OLSE: M = max_s lse_s, w_s = e^{lse_s - M}, O = sum w_s o_s / sum w_s,
 //         LSE = M + ln(sum w_s)
-//
-// A row of D floats is read by D/4 lanes, 16 bytes each. SG groups of such
-// lanes split the S splits among themselves (split s goes to group s % SG),
-// so a row uses 32*SG (D = 128) threads and all of a row's loads are
-// independent. Each thread folds its splits in one pass, rebasing its running
-// sums whenever a larger maximum arrives (the same merge applied one split at
-// a time); the SG partial states are then merged the same way through LDS.
-// A split whose m (lse) is -inf weighs exactly 0; a row whose splits are all
-// empty writes O = 0 and LSE = -inf. The order of every sum is fixed, so the
-// result is bitwise reproducible for a fixed plan.
+// Each row gets 32*SG threads (D = 128; 16*SG for D = 64) so all of a row's
+// loads are independent; see merge_rows.h for the per-lane fold and the
+// combination of the SG partial states.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "fd_internal.h"
+#include "merge_rows.h"
 
 namespace fd {
 namespace {
 
 constexpr int NT = 256;   // threads per workgroup
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p, int sg_log2) {
@@ -40,64 +32,30 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p, int sg_log2) {
   const int dl = t - grp * LPR;
   const int row = blockIdx.x * rpw + rl;
   const bool active = row < p.BH;
-  const int S = p.S;
   const bool uml = p.ws_format == FD_WS_UML;
-  const int sstride = uml ? 2 : 1;
 
-  __shared__ f32x4 part[NT];
+  __shared__ mf32x4 part[NT];
   __shared__ float part_m[NT];
   __shared__ float part_d[NT];
 
-  float M = -INFINITY, den = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    const float* stats = p.ws_stats + (int64_t)row * S * sstride;
-    const float* ws = p.ws_o + (int64_t)row * S * D + dl * 4;
-#pragma unroll 4
-    for (int s = grp; s < S; s += SG) {
-      const float ms = stats[s * sstride];
-      const float ls = uml ? stats[s * sstride + 1] : 1.f;
-      const f32x4 u = *reinterpret_cast<const f32x4*>(ws + (int64_t)s * D);
-      const bool valid = ms != -INFINITY;
-      const float mn = valid ? fmaxf(M, ms) : M;
-      const float a = M == -INFINITY ? 0.f : expf(M - mn);
-      const float w = valid ? expf(ms - mn) : 0.f;
-      acc = acc * a + u * w;
-      den = den * a + ls * w;
-      M = mn;
-    }
-  }
-  part[threadIdx.x] = acc;
-  part_m[threadIdx.x] = M;
-  part_d[threadIdx.x] = den;
+  RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
+  if (active)
+    st = fold_splits<D>(p.ws_o + (int64_t)row * p.S * D + dl * 4, p.ws_stats + (int64_t)row * p.S * (uml ? 2 : 1),
+                        p.S, uml, grp, SG);
+  part[threadIdx.x] = st.acc;
+  part_m[threadIdx.x] = st.m;
+  part_d[threadIdx.x] = st.den;
   __syncthreads();
-
   if (!active || grp != 0) return;
-  const int base = rl * tpr + dl;
-  float Mr = -INFINITY;
-  for (int g = 0; g < SG; ++g) Mr = fmaxf(Mr, part_m[base + g * LPR]);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float dr = 0.f;
-  if (Mr != -INFINITY) {
-    for (int g = 0; g < SG; ++g) {
-      const float mg = part_m[base + g * LPR];
-      const float a = mg == -INFINITY ? 0.f : expf(mg - Mr);
-      o += part[base + g * LPR] * a;
-      dr += part_d[base + g * LPR] * a;
-    }
-  }
-  const bool empty = !(dr > 0.f);
-  const float inv = empty ? 0.f : 1.f / dr;
-  *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + dl * 4) = o * inv;
-  if (p.lse && dl == 0) p.lse[row] = empty ? -INFINITY : Mr + logf(dr);
+  finish_row(part, part_m, part_d, rl * tpr + dl, LPR, SG, p.out + (int64_t)row * D, dl,
+             p.lse ? p.lse + row : nullptr);
 }
 
 }  // namespace
 
 int launch_merge(const MergeParams& p, int head_dim, void* stream) {
   const int lpr = head_dim / 4;
-  int sg_log2 = 0;
-  while ((1 << sg_log2) < p.S && (lpr << (sg_log2 + 1)) <= NT) ++sg_log2;
+  const int sg_log2 = split_groups_log2(p.S, lpr, 1, NT);
   const int rows_per_wg = NT / (lpr << sg_log2);
   dim3 grid((p.BH + rows_per_wg - 1) / rows_per_wg);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

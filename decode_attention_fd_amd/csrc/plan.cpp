@@ -3,14 +3,20 @@
 //
 // The split-count rule is the wave-efficiency rule of "Flash-Decoding:
 // Split-KV Attention for Long-Context Decode" (kanthi.in) §6: S = 1 when the
-// work units already fill 80 % of the resident slots; otherwise, among split
-// counts that change the number of blocks per split, the smallest whose
-// last-wave efficiency reaches 85 % of the best. The MI355X variant counts
-// slots as CUs x resident split workgroups per CU, counts blocks in units of
-// one workgroup iteration, and drops split counts whose fp32 workspace
-// traffic (written by the split kernel and read back by the merge) exceeds a
-// budget of the KV bytes -- the overhead check at the end of §6, generalised
-// to g query heads per KV head.
+// work units already fill 80 % of the slots; otherwise, among split counts
+// that change the number of blocks per split, the smallest whose last-wave
+// efficiency reaches a threshold of the best (85 % on the page).
+//
+// The MI355X variant is the same rule re-derived for a bandwidth-bound
+// kernel on 256 CUs: one split workgroup per CU (4 waves, two 32-token tiles
+// in flight each) already pulls that CU's share of HBM bandwidth, so a wave
+// of work is CUs x 1 workgroups, and any idle CU in the last wave costs
+// bandwidth directly, so the threshold is the best efficiency itself. Blocks
+// are one workgroup iteration (4 waves x 32 tokens); chunks are rounded to the
+// 32-token wave tile only. Split counts whose fp32 workspace traffic (written
+// by the split kernel and read back by the merge) exceeds a budget of the KV
+// bytes are dropped -- the overhead check at the end of §6, generalised to g
+// query heads per KV head.
 #include <math.h>
 #include <string.h>
 
@@ -39,7 +45,7 @@ double ws_ratio(int s, int g, int d, int elt, int64_t max_len) {
 
 // kanthi.in §6 rule; with budget < 0 no traffic bound is applied.
 int split_rule(int64_t work, int64_t slots, int64_t n_blocks, int max_splits, int g, int d, int elt,
-               int64_t max_len, double budget) {
+               int64_t max_len, double budget, double threshold) {
   if ((double)work >= 0.8 * (double)slots) return 1;
   int64_t cap = max_splits;
   if (slots < cap) cap = slots;
@@ -55,7 +61,7 @@ int split_rule(int64_t work, int64_t slots, int64_t n_blocks, int max_splits, in
   for (int s = 1; s <= cap; ++s) {
     if (!eligible(s, n_blocks)) continue;
     if (s > 1 && budget >= 0.0 && ws_ratio(s, g, d, elt, max_len) > budget) continue;
-    if (wave_eff(work, s, slots) >= 0.85 * best) return s;
+    if (wave_eff(work, s, slots) >= threshold * best) return s;
   }
   return 1;
 }
@@ -172,21 +178,23 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
   } else {
     const int max_splits = o->max_splits > 0 ? o->max_splits : 128;
     const int64_t work = (int64_t)prob->batch * prob->num_kv_heads;
-    int64_t block;
-    double budget;
+    int64_t block, align;
+    double budget, threshold;
     if (o->heuristic == FD_HEURISTIC_FA2) {
       slots = 2 * (int64_t)o->num_cus;
       block = 128;
+      align = block > paged_align ? block : paged_align;
       budget = -1.0;
+      threshold = 0.85;
     } else {
       slots = (int64_t)o->num_cus * o->wgs_per_cu;
       block = (int64_t)tile * waves;
+      align = tile > paged_align ? tile : paged_align;
       budget = o->overhead_budget > 0.0f ? (double)o->overhead_budget : 0.02;
+      threshold = 1.0;
     }
     const int64_t n_blocks = max_len > 0 ? cdiv64(max_len, block) : 0;
-    S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget);
-    int64_t align = block > paged_align ? block : paged_align;
-    if (paged && align % paged_align) align = paged_align;   // both are powers of two
+    S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget, threshold);
     chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
     S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
   }
@@ -209,6 +217,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
   const int64_t heads = (int64_t)prob->batch * prob->num_q_heads;
   out->ws_o_bytes = heads * S * D * 4;
   out->ws_stats_bytes = heads * S * (o->ws_format == FD_WS_UML ? 2 : 1) * 4;
+  out->ws_counter_bytes = (int64_t)prob->batch * prob->num_kv_heads * 4;
   out->prob = *prob;
   out->checksum = plan_checksum(out);
   return FD_OK;

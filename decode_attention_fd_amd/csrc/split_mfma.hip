@@ -14,8 +14,9 @@
 //   * K and V rows are fetched with fully coalesced 16-byte nontemporal loads
 //     (a wave instruction reads whole rows; the address is one scalar base per
 //     instruction plus a constant lane offset; every byte is read once, so the
-//     loads are marked streaming) into registers, two tiles ahead of use, and
-//     written to the wave's own LDS slice. Rows are padded by 16
+//     loads are marked streaming) into registers, one tile ahead of use, and
+//     written to the wave's own LDS slice; K and V are staggered so the wave
+//     always has loads in flight. Rows are padded by 16
 //     bytes so the 16 rows one MFMA operand read touches fall in distinct bank
 //     groups, while every LDS access is one base register plus an immediate.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 tokens x 32 dims of
@@ -36,6 +37,7 @@
 #include <math.h>
 
 #include "fd_internal.h"
+#include "merge_rows.h"
 
 namespace fd {
 namespace {
@@ -155,9 +157,9 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
     return pid;
   };
 
-  // Loads of the tile starting at t0 into (kr, vr). Instruction i reads rows
+  // Loads of one tensor's tile starting at t0 into r. Instruction i reads rows
   // t0 + i*RPI + [0, RPI); rows past `end` (tail tile only) re-read row end-1.
-  auto issue = [&](u32x4 (&kr)[G::NI], u32x4 (&vr)[G::NI], int t0, int pids) {
+  auto issue = [&](u32x4 (&r)[G::NI], const char* base, int t0, int pids) {
     const bool full = t0 + TT <= end;               // wave-uniform
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
@@ -176,20 +178,16 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
         const int tc = t < end - 1 ? t : end - 1;
         loff = (uint32_t)((tc - tu) * row_stride) + lchunk * 16;
       }
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + ubase + loff));
-      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + ubase + loff));
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + ubase + loff));
     }
   };
 
   unsigned char* ldsK = lds[wave][0];
   unsigned char* ldsV = lds[wave][1];
-  auto store = [&](const u32x4 (&kr)[G::NI], const u32x4 (&vr)[G::NI]) {
+  auto store = [&](const u32x4 (&r)[G::NI], unsigned char* dst) {
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-      const int off = (i * G::RPI + lrow) * G::ROWP + lchunk * 16;
-      *reinterpret_cast<u32x4*>(ldsK + off) = kr[i];
-      *reinterpret_cast<u32x4*>(ldsV + off) = vr[i];
-    }
+    for (int i = 0; i < G::NI; ++i)
+      *reinterpret_cast<u32x4*>(dst + (i * G::RPI + lrow) * G::ROWP + lchunk * 16) = r[i];
   };
 
   f32x4 oacc[G::NDB];
@@ -273,37 +271,31 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
     }
   };
 
-  // Two register buffers: tiles t and t + NW are in flight while tile t - NW is
-  // consumed from LDS. Tile indices past the split are clamped to its last tile
-  // (a reload that hits in cache), so every load is unconditional.
+  // One register tile per tensor, staggered: the K tile is stored and the next
+  // K tile requested before the V tile is stored and the next V tile
+  // requested, so this wave always has loads in flight while it writes LDS and
+  // while it computes. Tile indices past the split are clamped to its last
+  // tile (a reload that hits in cache), so every load is unconditional.
   const int last = ntiles - 1;
   auto tstart = [&](int tile) { return start + (tile < last ? tile : last) * TT; };
   if (ntiles > 0) {
-    u32x4 ka[G::NI], va[G::NI], kb2[G::NI], vb2[G::NI];
+    u32x4 kr[G::NI], vr[G::NI];
     int tile = wave;
-    int pid_a = 0, pid_b = 0;
-    if (PAGED) {
-      pid_a = page_ids(tstart(tile));
-      pid_b = page_ids(tstart(tile + NW));
-    }
-    issue(ka, va, tstart(tile), pid_a);
-    issue(kb2, vb2, tstart(tile + NW), pid_b);
-    if (PAGED) {
-      pid_a = page_ids(tstart(tile + 2 * NW));
-      pid_b = page_ids(tstart(tile + 3 * NW));
-    }
+    int pid = 0, pid_next = 0;
+    if (PAGED) pid = page_ids(tstart(tile));
+    issue(kr, kbase, tstart(tile), pid);
+    issue(vr, vbase, tstart(tile), pid);
+    if (PAGED) pid_next = page_ids(tstart(tile + NW));
     // One exit at the bottom: the wait-count analysis then sees the same load
-    // order (A older than B) on entry and on the back edge.
+    // order on entry and on the back edge.
     const int my_tiles = (ntiles - wave + NW - 1) / NW;     // > 0 only if wave < ntiles
-    for (int it = 0; it < (my_tiles + 1) / 2; ++it, tile += 2 * NW) {
-      store(ka, va);
-      issue(ka, va, tstart(tile + 2 * NW), pid_a);
-      if (PAGED) pid_a = page_ids(tstart(tile + 4 * NW));
+    for (int it = 0; it < my_tiles; ++it, tile += NW) {
+      store(kr, ldsK);
+      issue(kr, kbase, tstart(tile + NW), pid_next);
+      store(vr, ldsV);
+      issue(vr, vbase, tstart(tile + NW), pid_next);
+      if (PAGED) pid_next = page_ids(tstart(tile + 2 * NW));
       compute(start + tile * TT);
-      store(kb2, vb2);
-      issue(kb2, vb2, tstart(tile + 3 * NW), pid_b);
-      if (PAGED) pid_b = page_ids(tstart(tile + 5 * NW));
-      if (tile + NW < ntiles) compute(start + (tile + NW) * TT);
     }
   }
 
@@ -345,18 +337,20 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
       }
     }
     const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + s;
+    const bool co = p.fused != 0;
     if (p.ws_format == FD_WS_UML) {
-      p.ws_o[base * D + d] = U;
+      ws_store(p.ws_o + base * D + d, U, co);
       if (d == 0) {
-        p.ws_stats[base * 2] = M == -INFINITY ? -INFINITY : M * LN2;
-        p.ws_stats[base * 2 + 1] = L;
+        ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
+        ws_store(p.ws_stats + base * 2 + 1, L, co);
       }
     } else {
       const bool empty = !(L > 0.f);
-      p.ws_o[base * D + d] = empty ? 0.f : U / L;
-      if (d == 0) p.ws_stats[base] = empty ? -INFINITY : (M + log2f(L)) * LN2;
+      ws_store(p.ws_o + base * D + d, empty ? 0.f : U / L, co);
+      if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
+  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh);
 }
 
 template <int D, typename T, bool PAGED>

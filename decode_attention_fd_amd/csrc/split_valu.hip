@@ -18,6 +18,7 @@
 #include <math.h>
 
 #include "fd_internal.h"
+#include "merge_rows.h"
 
 namespace fd {
 namespace {
@@ -311,18 +312,20 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
         }
     }
     const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + s;
+    const bool co = p.fused != 0;
     if (p.ws_format == FD_WS_UML) {
-      p.ws_o[base * D + d] = Uv;
+      ws_store(p.ws_o + base * D + d, Uv, co);
       if (d == 0) {
-        p.ws_stats[base * 2] = M == -INFINITY ? -INFINITY : M * LN2;
-        p.ws_stats[base * 2 + 1] = L;
+        ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
+        ws_store(p.ws_stats + base * 2 + 1, L, co);
       }
     } else {
       const bool empty = !(L > 0.f);
-      p.ws_o[base * D + d] = empty ? 0.f : Uv / L;
-      if (d == 0) p.ws_stats[base] = empty ? -INFINITY : (M + log2f(L)) * LN2;
+      ws_store(p.ws_o + base * D + d, empty ? 0.f : Uv / L, co);
+      if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
+  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh);
 }
 
 template <int D, typename T, int G>

@@ -90,9 +90,11 @@ typedef enum {
 } fd_kernel;
 
 typedef enum {
-  /* Wave-efficiency rule of kanthi.in §6 on slots = CUs x resident
-   * workgroups per CU, restricted to split counts whose workspace traffic
-   * stays within overhead_budget of the KV bytes (§6 overhead check). */
+  /* Wave-efficiency rule of kanthi.in §6 re-derived for a bandwidth-bound
+   * kernel on MI355X: slots = CUs x wgs_per_cu (1 by default), the smallest
+   * split count reaching the best last-wave efficiency, chunks rounded to the
+   * 32-token wave tile, and only split counts whose workspace traffic stays
+   * within overhead_budget of the KV bytes (§6 overhead check). */
   FD_HEURISTIC_MI355X = 0,
   /* The §6 rule exactly as printed: slots = 2 x CUs, block = 128 tokens, no
    * traffic bound. Kept to reproduce the page's table. */
@@ -131,7 +133,9 @@ typedef struct {
 /* Planner options. Zero-initialise for the defaults. */
 typedef struct {
   int32_t num_cus;            /* 0: ask the current device (hipGetDeviceProperties) */
-  int32_t wgs_per_cu;         /* 0: the chosen kernel's resident workgroups per CU */
+  int32_t wgs_per_cu;         /* split workgroups per CU in one wave of the MI355X rule; 0: 1
+                                 (one streaming workgroup per CU saturates its HBM share);
+                                 clamped to the kernel's resident workgroups per CU */
   int32_t force_splits;       /* > 0: use this many splits (0 = heuristic, FA2's num_splits=0) */
   int32_t force_chunk_tokens; /* > 0: tokens per split (e.g. 1024); S = cdiv(max_seq_len, chunk) */
   int32_t ws_format;          /* fd_ws_format */
@@ -153,12 +157,13 @@ typedef struct {
   int32_t group;              /* g = Hq / Hkv */
   int32_t tile_tokens;        /* KV tokens one wave consumes per loop iteration */
   int32_t waves_per_wg;       /* waves per split workgroup */
-  int32_t slots;              /* CUs x resident workgroups per CU used by the heuristic */
+  int32_t slots;              /* workgroup slots of one wave in the split rule */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (S, Hkv, B) */
   float scale;                /* resolved score scale */
   int32_t reserved1;
   int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
   int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
+  int64_t ws_counter_bytes;   /* uint32 [B, Hkv] arrival counters of fd_decode_fused */
   fd_problem prob;            /* copy of the problem */
   uint64_t checksum;          /* over the fields above */
 } fd_plan_t;
@@ -194,6 +199,20 @@ FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args,
  * out: float [B, Hq, D] contiguous; lse: float [B, Hq] or NULL. */
 FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats,
                     float* out, float* lse, void* stream);
+
+/* Split kernel with the merge fused in: as fd_decode_split, and in addition the
+ * workgroup that finishes last for each (sequence, KV head) merges that
+ * group's split states and writes out/lse as fd_merge would (kanthi.in §9
+ * decode contract names this "documented fused alternative"; its "Try this"
+ * list describes the last-CTA merge with an atomic counter). One launch
+ * instead of two. counters: uint32 [B * Hkv] (plan->ws_counter_bytes), all
+ * zero before the first call (allocate it zeroed); every call leaves them
+ * zero again. Calls that share counters or workspace must not overlap in
+ * time (issue them on one stream). out: float [B, Hq, D]; lse: float [B, Hq]
+ * or NULL. */
+FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes,
+                           float* ws_stats, size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes,
+                           float* out, float* lse, void* stream);
 
 /* Human-readable text for an fd_status. Never NULL. */
 FD_API const char* fd_status_str(int status);

@@ -65,9 +65,12 @@ def workspace_ratio(splits: int, group: int, head_dim: int, kv_elt: int, max_len
 
 
 def num_splits_traffic(work: int, slots: int, n_blocks: int, max_splits: int, group: int,
-                       head_dim: int, kv_elt: int, max_len: int, budget: float) -> int:
+                       head_dim: int, kv_elt: int, max_len: int, budget: float,
+                       threshold: float = 0.85) -> int:
     """The §6 rule restricted to split counts whose workspace traffic stays within
-    ``budget`` of the KV bytes (S = 1 is always allowed). Parity unpinned."""
+    ``budget`` of the KV bytes (S = 1 is always allowed), taking the smallest
+    split count whose efficiency reaches ``threshold`` of the best (the page
+    uses 0.85). Parity unpinned."""
     if work >= 0.8 * slots:
         return 1
     cap = min(max_splits, slots, n_blocks)
@@ -77,7 +80,7 @@ def num_splits_traffic(work: int, slots: int, n_blocks: int, max_splits: int, gr
              and (s == 1 or workspace_ratio(s, group, head_dim, kv_elt, max_len) <= budget)]
     eff = {s: wave_efficiency(work, s, slots) for s in cands}
     best = max(eff.values())
-    return min(s for s in cands if eff[s] >= 0.85 * best)
+    return min(s for s in cands if eff[s] >= threshold * best)
 
 
 def chunk_for(max_len: int, splits: int, align: int) -> int:

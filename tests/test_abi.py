@@ -95,8 +95,9 @@ def test_fa2_heuristic_reproduces_page_table():
 
 
 @pytest.mark.parametrize("kernel", ["mfma", "valu"])
-def test_mi355x_heuristic_matches_oracle_rule(kernel):
-    cus, wgs = 256, 2
+@pytest.mark.parametrize("wgs", [1, 2])
+def test_mi355x_heuristic_matches_oracle_rule(kernel, wgs):
+    cus = 256
     budget = 0.02
     for B in (1, 2, 4, 16, 64):
         for Hkv, g in ((8, 8), (8, 4), (32, 1), (2, 2)):
@@ -106,11 +107,21 @@ def test_mi355x_heuristic_matches_oracle_rule(kernel):
                 prob = contiguous_problem(B=B, Hq=Hkv * g, Hkv=Hkv, L=L)
                 plan = fd.fd_plan(prob, num_cus=cus, wgs_per_cu=wgs, kernel=kernel)
                 block = plan.tile_tokens * plan.waves_per_wg
-                s = OP.num_splits_traffic(B * Hkv, cus * wgs, math.ceil(L / block), 128, g, 128, 2, L, budget)
-                chunk = OP.chunk_for(L, s, block)
+                s = OP.num_splits_traffic(B * Hkv, cus * wgs, math.ceil(L / block), 128, g, 128, 2, L, budget,
+                                          threshold=1.0)
+                chunk = OP.chunk_for(L, s, plan.tile_tokens)
                 assert plan.chunk_tokens == chunk, (B, Hkv, g, L)
                 assert plan.num_splits == math.ceil(L / chunk), (B, Hkv, g, L)
                 assert plan.num_splits <= s
+
+
+def test_mi355x_choices_for_the_workloads():
+    """The planner's picks for the four large workloads (256 CUs, defaults)."""
+    assert fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256).num_splits == 32
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256)
+    assert p.chunk_tokens == 4000 and p.slots == 256
+    assert fd.fd_plan(contiguous_problem(B=64, Hq=32, Hkv=8, L=2048), num_cus=256).num_splits == 1
+    assert fd.fd_plan(contiguous_problem(Hq=32, Hkv=32, L=65536, dtype=2), num_cus=256).num_splits == 8
 
 
 def test_forced_splits_and_chunk():

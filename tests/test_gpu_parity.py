@@ -252,3 +252,66 @@ def test_occupancy_table_matches_device():
         H.say(f"{hq}/{hkv} D{d} {dt} page={page}: CUs {props.multi_processor_count} device slots "
               f"{dev_plan.slots} table slots {host_plan.slots}")
         assert dev_plan.slots == host_plan.slots
+
+
+# ---------------------------------------------------------------------------
+# Fused merge (one launch): last workgroup per (sequence, KV head) merges
+# ---------------------------------------------------------------------------
+
+def _run_fused(w, ctr=None, **over):
+    dev = torch.device("cuda", 0)
+    q, k, v, sl = w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev)
+    bt = None if w.block_table is None else w.block_table.to(dev)
+    opts = H.plan_opts_for(w, **over)
+    H.say(f"fused {w.name} opts={opts}")
+    plan = fd.fd_plan(fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale), **opts)
+    ws_o, ws_stats = fd.workspace(plan, dev)
+    ctr = fd.counters(plan, dev) if ctr is None else ctr
+    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse, bt)
+    torch.cuda.synchronize()
+    return plan, out.cpu(), lse.cpu(), ctr
+
+
+@pytest.mark.parametrize("case", ["gqa_f16", "mha_bf16_valu", "paged", "tiny_f32", "zero_rows"])
+def test_fused_matches_oracle(case):
+    if case == "gqa_f16":
+        w, opts = W.contiguous("fused_gqa", seed=80, batch=2, q_heads=32, kv_heads=4, head_dim=128, capacity=5000,
+                               seq_lens=[5000, 1111], dtype="f16"), {}
+    elif case == "mha_bf16_valu":
+        w, opts = W.contiguous("fused_mha", seed=81, batch=2, q_heads=4, kv_heads=4, head_dim=128, capacity=3000,
+                               seq_lens=[3000, 5], dtype="bf16"), {"force_splits": 7, "ws_format": "olse"}
+    elif case == "paged":
+        w, opts = W.paged("fused_paged", seed=82, batch=3, q_heads=16, kv_heads=4, head_dim=128,
+                          seq_lens=[2000, 17, 700], page_size=16, dtype="f16"), {"force_splits": 5}
+    elif case == "tiny_f32":
+        w, opts = W.ragged_mha_f32(num_splits=8), {}
+    else:
+        w, opts = W.contiguous("fused_zero", seed=83, batch=3, q_heads=8, kv_heads=2, head_dim=64, capacity=300,
+                               seq_lens=[0, 300, 0], dtype="f16"), {"force_splits": 3}
+    plan, out, lse, ctr = _run_fused(w, **opts)
+    assert torch.all(ctr == 0).item(), "counters must be back at zero"
+    H.check_against_oracle(w, out, lse)
+
+
+def test_fused_repeated_calls_reset_counters():
+    w1 = W.contiguous("fused_rep1", seed=84, batch=2, q_heads=16, kv_heads=2, head_dim=128, capacity=4000,
+                      seq_lens=[4000, 2500], dtype="f16")
+    w2 = W.contiguous("fused_rep2", seed=85, batch=2, q_heads=16, kv_heads=2, head_dim=128, capacity=4000,
+                      seq_lens=[3333, 4000], dtype="f16")
+    plan, out1, lse1, ctr = _run_fused(w1, force_splits=9)
+    _, out2, lse2, ctr = _run_fused(w2, ctr=ctr, force_splits=9)
+    _, out3, lse3, ctr = _run_fused(w1, ctr=ctr, force_splits=9)
+    H.check_against_oracle(w1, out1, lse1)
+    H.check_against_oracle(w2, out2, lse2)
+    assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
+
+
+def test_fused_agrees_with_two_launch_path():
+    w = W.contiguous("fused_vs_split", seed=86, batch=1, q_heads=64, kv_heads=8, head_dim=128, capacity=20000,
+                     seq_lens=[20000], dtype="f16")
+    _, out_f, lse_f, _ = _run_fused(w)
+    _, out_s, lse_s, _, _ = H.run(w)
+    assert (out_f - out_s).abs().max().item() < 1e-5
+    assert (lse_f - lse_s).abs().max().item() < 1e-5
