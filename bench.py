@@ -77,6 +77,46 @@ def traffic_from_profile(workload: str, kernel_hash: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def _pmc_rows(d: str, counter: str):
+    """(kernel name, counter value) per dispatch from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> None:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, scaled by the
+    same counters on the calibration copy (COPY_BYTES read and written)."""
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d, counter)
+        split = [v for n, v in rows if "split_" in n and "kernel" in n]
+        copy = [v for n, v in rows if "copyBuffer" in n]     # the runtime's device-to-device copy kernel
+        if not split or not copy:
+            raise SystemExit(f"{counter}: no split-kernel or copy dispatches in {d}")
+        split_kib = sum(split) / len(split)
+        copy_kib = max(copy)                     # the 256 MiB calibration copy is the largest one
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[key] = {"counter": counter, "split_kib_per_dispatch": split_kib, "split_dispatches": len(split),
+                    "copy_kib_per_dispatch": copy_kib, "scale": factor,
+                    "bytes_per_launch": split_kib * 1024.0 * factor}
+    out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    path = os.path.join(ROOT, "profiles", f"traffic_split_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, max_heads: int):
     """Time the float64 oracle on the host over the first `max_heads` (b, hq)
     pairs of copy 0 and scale to the whole step; returns the JSON object."""
@@ -120,7 +160,15 @@ def main():
     ap.add_argument("--path", choices=["fused", "split"], default="fused",
                     help="fused: one launch (last workgroup per group merges); split: split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench into "
+                         "profiles/traffic_split_<workload>.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs the decode on a single device "
@@ -198,6 +246,13 @@ def main():
     merge_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     split_us = sum(split_ms) / len(split_ms) * 1e3
     merge_us = sum(merge_ms) / len(merge_ms) * 1e3
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     tbps = step_kv / (us_step * 1e-6) / 1e12
     achieved = step_kv / (split_us * 1e-6) / 1e9
