@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
     ap.add_argument("--path", choices=["fused", "split"], default="fused",
                     help="fused: one launch (last workgroup per group merges); split: split + merge kernels")
+    ap.add_argument("--schedule", choices=["auto", "uniform", "balanced"], default="auto",
+                    help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
+    ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner slots per CU (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
@@ -199,6 +202,11 @@ def main():
         opts["force_splits"] = w0.num_splits
     if w0.chunk_tokens and not args.splits:
         opts["force_chunk_tokens"] = w0.chunk_tokens
+    if "force_splits" not in opts and "force_chunk_tokens" not in opts:
+        opts["host_seq_lens"] = w0.seq_lens.cpu().tolist()   # length-aware split plan
+        opts["schedule"] = args.schedule
+    if args.wgs_per_cu:
+        opts["wgs_per_cu"] = args.wgs_per_cu
     prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
     t0 = time.perf_counter()
     plan = fd.fd_plan(prob, **opts)
@@ -280,6 +288,7 @@ def main():
             "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
             "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
             "slots": plan.slots, "plan_us": round(plan_us, 1), "path": args.path,
+            "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "grid": plan.grid_x * plan.grid_y * plan.grid_z,
         },
         "split_kernel_us": round(split_us, 2),
         "merge_kernel_us": round(merge_us, 2),

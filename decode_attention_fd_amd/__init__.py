@@ -29,6 +29,7 @@ LAYOUT_CONTIGUOUS, LAYOUT_PAGED = 0, 1
 WS_FORMATS = {"uml": 0, "olse": 1}
 KERNELS = {"auto": 0, "mfma": 1, "valu": 2}
 HEURISTICS = {"mi355x": 0, "fa2": 1}
+SCHEDULES = {"auto": 0, "uniform": 1, "balanced": 2}
 PLAN_MAGIC = 0x46445031
 
 
@@ -52,7 +53,8 @@ class PlanOpts(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("force_splits", ctypes.c_int32),
         ("force_chunk_tokens", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("kernel", ctypes.c_int32),
         ("heuristic", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("overhead_budget", ctypes.c_float),
-        ("reserved", ctypes.c_int32 * 7),
+        ("num_host_seq_lens", ctypes.c_int32), ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
+        ("host_seq_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -62,7 +64,7 @@ class Plan(ctypes.Structure):
         ("kernel", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("group", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("slots", ctypes.c_int32),
         ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
-        ("scale", ctypes.c_float), ("reserved1", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("schedule", ctypes.c_int32),
         ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64), ("ws_counter_bytes", ctypes.c_int64),
         ("prob", Problem), ("checksum", ctypes.c_uint64),
     ]
@@ -184,9 +186,17 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: tor
 
 def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_splits: int = 0,
             force_chunk_tokens: int = 0, ws_format: str = "uml", kernel: str = "auto",
-            heuristic: str = "mi355x", max_splits: int = 0, overhead_budget: float = 0.0) -> Plan:
-    """Call ``fd_plan``. ``num_cus=0`` asks the current device."""
+            heuristic: str = "mi355x", max_splits: int = 0, overhead_budget: float = 0.0,
+            host_seq_lens=None, schedule: str = "auto") -> Plan:
+    """Call ``fd_plan``. ``num_cus=0`` asks the current device. ``host_seq_lens``
+    (a host list / CPU tensor of the batch's lengths) enables length-aware
+    splits and the balanced schedule."""
     o = PlanOpts()
+    keep = None
+    if host_seq_lens is not None:
+        keep = (ctypes.c_int32 * len(host_seq_lens))(*[int(x) for x in host_seq_lens])
+        o.num_host_seq_lens = len(host_seq_lens)
+        o.host_seq_lens = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
     o.num_cus, o.wgs_per_cu = num_cus, wgs_per_cu
     o.force_splits, o.force_chunk_tokens = force_splits, force_chunk_tokens
     o.ws_format = WS_FORMATS[ws_format]
@@ -194,8 +204,10 @@ def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_sp
     o.heuristic = HEURISTICS[heuristic]
     o.max_splits = max_splits
     o.overhead_budget = overhead_budget
+    o.schedule = SCHEDULES[schedule]
     plan = Plan()
     _check(lib().fd_plan(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(plan)), "fd_plan")
+    del keep
     return plan
 
 

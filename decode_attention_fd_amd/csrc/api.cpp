@@ -63,6 +63,9 @@ int check_plan(const fd_plan_t* plan) {
   if (plan->magic != FD_PLAN_MAGIC || plan->checksum != plan_checksum(plan)) return FD_ERR_BAD_PLAN;
   if (validate_problem(&plan->prob) != FD_OK) return FD_ERR_BAD_PLAN;
   if (plan->num_splits < 1 || plan->chunk_tokens < 1) return FD_ERR_BAD_PLAN;
+  if (plan->schedule != FD_SCHEDULE_UNIFORM && plan->schedule != FD_SCHEDULE_BALANCED) return FD_ERR_BAD_PLAN;
+  if (plan->schedule == FD_SCHEDULE_BALANCED && (plan->kernel != FD_KERNEL_MFMA || plan->grid_x < 1))
+    return FD_ERR_BAD_PLAN;
   return FD_OK;
 }
 
@@ -189,9 +192,14 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
   } else {
     p.cap_tokens = pr.kv_capacity;
   }
-  // Tokens past S*chunk belong to no split: clamp there as well.
-  const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;
-  if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
+  if (plan->schedule == FD_SCHEDULE_BALANCED) {
+    p.nwg = plan->grid_x;
+    p.granule = plan->chunk_tokens;
+  } else {
+    // Tokens past S*chunk belong to no split: clamp there as well.
+    const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;
+    if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
+  }
   p.ws_format = plan->ws_format;
   p.scale_log2 = (float)((double)plan->scale * 1.4426950408889634);
   return FD_OK;

@@ -28,6 +28,9 @@ struct SplitParams {
   int32_t page_log2, num_pages;
   int32_t ws_format;
   float scale_log2;                     // scale * log2(e): scores go straight to base 2
+  // balanced schedule (nwg = 0: uniform grid (S, Hkv, B))
+  int32_t nwg;                          // workgroups of the balanced grid
+  int32_t granule;                      // tokens per granule of the balanced line
   // fused merge (0 = write split states only)
   int32_t fused;
   uint32_t* counters;                   // [B * Hkv], zero on entry, zero on exit

@@ -128,15 +128,16 @@ __device__ __forceinline__ RowState fold_splits_coherent(const float* ws, const 
   return st;
 }
 
-// Fused merge at the end of a split workgroup (the "last CTA merges" variant of
+// Fused merge at the end of a split workgroup (or of one piece of it) (the "last CTA merges" variant of
 // the kanthi.in chapter's decode contract). Every workgroup of a (sequence,
 // KV head) group has written its split states with ws_store(..., true); once
 // its own stores have completed (s_waitcnt) the workgroup counts itself in
-// with a device-scope atomic, and the one that arrives last reads the group's
+// with a device-scope atomic, and the one that arrives as number `expected`
+// (the group's writer count) reads the group's
 // states back with device-coherent loads, merges the g rows into out/lse and
 // resets the counter to 0 so the next stream-ordered call starts from zero.
 template <int D, int NTHREADS>
-__device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, int kvh) {
+__device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, int kvh, int expected) {
   __shared__ int s_last;
   __shared__ mf32x4 part[NTHREADS];
   __shared__ float part_m[NTHREADS];
@@ -146,7 +147,7 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   if (threadIdx.x == 0) {
     const unsigned old = __hip_atomic_fetch_add(p.counters + (int64_t)b * p.Hkv + kvh, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (unsigned)(p.S - 1);
+    s_last = old == (unsigned)(expected - 1);
   }
   __syncthreads();
   if (!s_last) return;

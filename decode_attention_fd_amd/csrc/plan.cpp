@@ -148,6 +148,14 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
   if (o->ws_format != FD_WS_UML && o->ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
   if (o->heuristic != FD_HEURISTIC_MI355X && o->heuristic != FD_HEURISTIC_FA2) return FD_ERR_INVALID_ARG;
   if (!(o->overhead_budget >= 0.0f)) return FD_ERR_INVALID_ARG;
+  if (o->num_host_seq_lens < 0 || (o->num_host_seq_lens > 0 && !o->host_seq_lens)) return FD_ERR_INVALID_ARG;
+  if (o->num_host_seq_lens > 0 && o->num_host_seq_lens != prob->batch) return FD_ERR_INVALID_ARG;
+  if (o->schedule < FD_SCHEDULE_AUTO || o->schedule > FD_SCHEDULE_BALANCED) return FD_ERR_INVALID_ARG;
+  if (o->schedule == FD_SCHEDULE_BALANCED &&
+      (o->num_host_seq_lens == 0 || o->force_splits > 0 || o->force_chunk_tokens > 0))
+    return FD_ERR_INVALID_ARG;
+  for (int i = 0; i < o->num_host_seq_lens; ++i)
+    if (o->host_seq_lens[i] > prob->max_seq_len) return FD_ERR_INVALID_ARG;
 
   const int kernel = choose_kernel(prob, o->kernel);
   if (kernel < 0) return -kernel;
@@ -166,7 +174,56 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
 
   int64_t S = 1, chunk = 1;
   int64_t slots = 0;
-  if (o->force_chunk_tokens > 0) {
+  int64_t nwg = 0;                      // balanced grid (0: uniform)
+  // AUTO takes the balanced schedule where it pays: ragged lengths (equal
+  // lengths are already balanced by the uniform chunks) and no more segments
+  // than workgroup slots (a workgroup then meets about two segments; with
+  // many short segments per workgroup the pieces' start-up latencies, paid
+  // one after another, cost more than the balance gains).
+  bool ragged = false;
+  for (int b = 1; b < o->num_host_seq_lens; ++b) ragged |= o->host_seq_lens[b] != o->host_seq_lens[0];
+  const bool balanced =
+      o->schedule == FD_SCHEDULE_BALANCED ||
+      (o->schedule == FD_SCHEDULE_AUTO && o->num_host_seq_lens > 0 && o->force_splits <= 0 &&
+       o->force_chunk_tokens <= 0 && o->heuristic == FD_HEURISTIC_MI355X && ragged &&
+       (int64_t)prob->batch * prob->num_kv_heads <= (int64_t)o->num_cus * o->wgs_per_cu);
+  if (balanced) {
+    if (kernel != FD_KERNEL_MFMA) {
+      if (o->schedule == FD_SCHEDULE_BALANCED) return FD_ERR_UNSUPPORTED;
+    } else {
+      // The line of granules (see fd_schedule): N workgroups, range w =
+      // [floor(w T / N), floor((w + 1) T / N)); S = the most ranges that any
+      // one segment meets.
+      slots = (int64_t)o->num_cus * o->wgs_per_cu;
+      const int64_t G = tile > paged_align ? tile : paged_align;
+      const int64_t H = prob->num_kv_heads;
+      int64_t T = 0;
+      for (int b = 0; b < prob->batch; ++b) {
+        const int32_t n = o->host_seq_lens[b] > 0 ? o->host_seq_lens[b] : 0;
+        T += H * cdiv64(n, G);
+      }
+      nwg = T > 0 ? cdiv64(T, 4) : 1;
+      if (nwg > slots) nwg = slots;
+      if (nwg > 0x7fffffff) return FD_ERR_UNSUPPORTED;
+      auto owner = [&](int64_t x) { return ((x + 1) * nwg + T - 1) / T - 1; };
+      S = 1;
+      int64_t x = 0;
+      for (int b = 0; b < prob->batch; ++b) {
+        const int32_t n = o->host_seq_lens[b] > 0 ? o->host_seq_lens[b] : 0;
+        const int64_t plen = cdiv64(n, G);
+        for (int64_t h = 0; h < H && plen > 0; ++h) {
+          const int64_t ss = x + h * plen;
+          const int64_t c = owner(ss + plen - 1) - owner(ss) + 1;
+          if (c > S) S = c;
+        }
+        x += H * plen;
+      }
+      chunk = G;
+    }
+  }
+  if (nwg > 0) {
+    // planned above
+  } else if (o->force_chunk_tokens > 0) {
     chunk = o->force_chunk_tokens;
     if (chunk % paged_align) return FD_ERR_INVALID_ARG;
     S = o->force_splits > 0 ? o->force_splits : (max_len > 0 ? cdiv64(max_len, chunk) : 1);
@@ -193,9 +250,29 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
       budget = o->overhead_budget > 0.0f ? (double)o->overhead_budget : 0.02;
       threshold = 1.0;
     }
-    const int64_t n_blocks = max_len > 0 ? cdiv64(max_len, block) : 0;
-    S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget, threshold);
-    chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
+    if (o->heuristic == FD_HEURISTIC_MI355X && o->host_seq_lens && o->num_host_seq_lens > 0) {
+      // Length-aware: no split longer than one slot's share of the total work.
+      int64_t total = 0;
+      for (int i = 0; i < o->num_host_seq_lens; ++i) total += o->host_seq_lens[i] > 0 ? o->host_seq_lens[i] : 0;
+      total *= prob->num_kv_heads;
+      if (max_len <= 0) {
+        chunk = align;
+      } else {
+        chunk = cdiv64(cdiv64(total, slots), align) * align;
+        if (chunk < align) chunk = align;
+        for (;;) {
+          const int64_t s_try = cdiv64(max_len, chunk);
+          if (s_try <= (max_splits > 0 ? max_splits : 1) &&
+              (s_try == 1 || ws_ratio((int)s_try, g, D, elt, max_len) <= budget))
+            break;
+          chunk += align;
+        }
+      }
+    } else {
+      const int64_t n_blocks = max_len > 0 ? cdiv64(max_len, block) : 0;
+      S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget, threshold);
+      chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
+    }
     S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
   }
   if (S < 1 || S > 65535 || chunk < 1 || chunk > 0x7fffffff) return FD_ERR_UNSUPPORTED;
@@ -210,9 +287,10 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
   out->tile_tokens = tile;
   out->waves_per_wg = waves;
   out->slots = (int32_t)slots;
-  out->grid_x = (int32_t)S;
-  out->grid_y = prob->num_kv_heads;
-  out->grid_z = prob->batch;
+  out->schedule = nwg > 0 ? FD_SCHEDULE_BALANCED : FD_SCHEDULE_UNIFORM;
+  out->grid_x = nwg > 0 ? (int32_t)nwg : (int32_t)S;
+  out->grid_y = nwg > 0 ? 1 : prob->num_kv_heads;
+  out->grid_z = nwg > 0 ? 1 : prob->batch;
   out->scale = prob->scale != 0.0f ? prob->scale : (float)(1.0 / sqrt((double)D));
   const int64_t heads = (int64_t)prob->batch * prob->num_q_heads;
   out->ws_o_bytes = heads * S * D * 4;

@@ -38,6 +38,7 @@
 
 #include "fd_internal.h"
 #include "merge_rows.h"
+#include "balance.h"
 
 namespace fd {
 namespace {
@@ -89,29 +90,30 @@ __device__ __forceinline__ unsigned pick_half(unsigned a, unsigned b, int e) {
   return (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
+template <int D> struct Smem {
+  unsigned char lds[NW][2][Geo<D>::TILEB];
+  float st_m[NW][16];
+  float st_l[NW][16];
+};
+
+// Tokens [start, end) of segment (b, kvh), end > start, for the g query heads
+// of the group; the state goes to split slot `slot`.
 template <int D, typename T, bool PAGED>
-__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
+__device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, int b, int kvh, int start, int end,
+                                            int slot) {
   using G = Geo<D>;
   using V8 = typename Mma<T>::vec;
   using VR = typename VRead<G::VW>::type;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NW][2][G::TILEB];
-  __shared__ float st_m[NW][16];
-  __shared__ float st_l[NW][16];
+  auto& lds = sm.lds;
+  auto& st_m = sm.st_m;
+  auto& st_l = sm.st_l;
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
   const int col = lane & 15;     // MFMA column = query column
   const int grp = lane >> 4;     // 16-lane group
-
-  int seq_len = p.seq_lens[b];
-  seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
-  const int start = s * p.chunk;
-  const int end = min(start + p.chunk, seq_len);
-  const int ntiles = end > start ? (end - start + TT - 1) / TT : 0;
+  const int ntiles = (end - start + TT - 1) / TT;
 
   // ---- Q^T as the B operand of S^T = K Q^T: column col holds head h(col).
   const int hcol = col < g ? col : (col < 2 * g ? col - g : -1);
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
         L += a * st_l[w2][h];
       }
     }
-    const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + s;
+    const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + slot;
     const bool co = p.fused != 0;
     if (p.ws_format == FD_WS_UML) {
       ws_store(p.ws_o + base * D + d, U, co);
@@ -350,7 +352,45 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
       if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
-  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh);
+}
+
+// Uniform schedule: workgroup (s, kvh, b) owns split s of segment (b, kvh).
+template <int D, typename T, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
+  __shared__ Smem<D> sm;
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  int seq_len = p.seq_lens[b];
+  seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
+  const int start = s * p.chunk;
+  const int end = min(start + p.chunk, seq_len);
+  if (end > start)
+    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s);
+  else
+    write_neutral<D, NW * 64>(p, b, kvh, s, s + 1);
+  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+}
+
+// Balanced schedule: workgroup w owns an equal share of the batch's granules.
+template <int D, typename T, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParams p) {
+  __shared__ Smem<D> sm;
+  balanced_walk<NW * 64>(
+      p,
+      [&](int b, int kvh, int start, int end, int slot, int count, bool last) {
+        b = __builtin_amdgcn_readfirstlane(b);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        start = __builtin_amdgcn_readfirstlane(start);
+        end = __builtin_amdgcn_readfirstlane(end);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+        if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
+        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot);
+        if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
+        if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+        __syncthreads();                         // LDS is reused by the next piece
+      },
+      [&](int b) { empty_row<D, NW * 64>(p, b); });
 }
 
 template <int D, typename T, bool PAGED>
@@ -360,9 +400,11 @@ int occupancy(int* out) {
 
 template <int D, typename T, bool PAGED>
 int launch(const SplitParams& p, void* stream) {
-  dim3 grid(p.S, p.Hkv, p.B);
-  hipLaunchKernelGGL((split_mfma_kernel<D, T, PAGED>), grid, dim3(NW * 64), 0,
-                     reinterpret_cast<hipStream_t>(stream), p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (p.nwg > 0)
+    hipLaunchKernelGGL((split_mfma_balanced_kernel<D, T, PAGED>), dim3(p.nwg), dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((split_mfma_kernel<D, T, PAGED>), dim3(p.S, p.Hkv, p.B), dim3(NW * 64), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
       if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
-  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh);
+  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
 }
 
 template <int D, typename T, int G>

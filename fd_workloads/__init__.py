@@ -14,11 +14,16 @@ use standard-normal synthetic tensors). No dataset or trained weight is used.
 Layouts
 -------
 contiguous : K, V are ``[B, Hkv, T_cap, D]`` with ``d`` contiguous.
-paged      : K, V pools are ``[num_pages, page_size, Hkv, D]``; ``block_table``
-             is int32 ``[B, max_pages_per_seq]``; token ``t`` of sequence ``b``
-             lives in page ``block_table[b, t // page_size]`` at row
-             ``t % page_size``. Unused block-table entries are filled with a
-             valid page id (0) so that any read stays inside the pool.
+paged      : K, V pools are indexed ``[num_pages, page_size, Hkv, D]``;
+             ``block_table`` is int32 ``[B, max_pages_per_seq]``; token ``t``
+             of sequence ``b`` lives in page ``block_table[b, t // page_size]``
+             at row ``t % page_size``. Unused block-table entries are filled
+             with a valid page id (0) so that any read stays inside the pool.
+             The pool's storage order is either head-major ("hnd": memory
+             ``[page, head, token, D]``, one head's page contiguous, the
+             default) or token-major ("nhd": memory ``[page, token, head, D]``);
+             both are handed over as the same ``[P, page, Hkv, D]`` index
+             order and differ only in strides.
 """
 from __future__ import annotations
 
@@ -47,6 +52,7 @@ class Workload:
     ws_format: str = "uml"          # "uml" (u, m, l) or "olse" (o, lse)
     scale: float = 0.0              # 0 = 1/sqrt(D)
     k_gain: float = 1.0             # K was drawn as k_gain * N(0, 1)
+    pool_layout: str = ""           # paged only: "hnd" or "nhd" storage order
 
     @property
     def batch(self) -> int:
@@ -79,11 +85,13 @@ class Workload:
         return tokens * self.num_kv_heads * 2 * self.head_dim * elt
 
     def to(self, device) -> "Workload":
+        """Copy to ``device`` keeping every tensor's strides (pool storage order)."""
         moved = dataclasses.replace(self)
         for f in ("q", "k", "v", "seq_lens", "block_table"):
             t = getattr(self, f)
             if t is not None:
-                setattr(moved, f, t.to(device))
+                c = torch.empty_strided(tuple(t.shape), t.stride(), dtype=t.dtype, device=device)
+                setattr(moved, f, c.copy_(t))
         return moved
 
 
@@ -111,9 +119,19 @@ def contiguous(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int,
                     ws_format=ws_format, k_gain=k_gain)
 
 
+def _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, layout, gain=1.0):
+    """A K or V pool indexed [P, page, Hkv, D], drawn in its storage order."""
+    if layout == "hnd":
+        return _randn(gen, (num_pages, kv_heads, page_size, head_dim), dt, device, gain).permute(0, 2, 1, 3)
+    if layout == "nhd":
+        return _randn(gen, (num_pages, page_size, kv_heads, head_dim), dt, device, gain)
+    raise ValueError(f"unknown pool layout {layout!r}")
+
+
 def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head_dim: int,
           seq_lens, page_size: int = 16, dtype: str = "f16", device="cpu",
-          num_splits: int = 0, chunk_tokens: int = 0, extra_pages: int = 0) -> Workload:
+          num_splits: int = 0, chunk_tokens: int = 0, extra_pages: int = 0,
+          pool_layout: str = "hnd") -> Workload:
     """Paged-pool workload: the pool holds exactly sum_b cdiv(len_b, page) pages
     (+ ``extra_pages`` unused ones); a seeded ``randperm`` of the pool is dealt
     out to the sequences in order, so each sequence's pages are scattered."""
@@ -133,10 +151,11 @@ def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head
     gen = torch.Generator(device=device)
     gen.manual_seed(seed + 1000)
     q = _randn(gen, (batch, q_heads, head_dim), dt, device)
-    k = _randn(gen, (num_pages, page_size, kv_heads, head_dim), dt, device)
-    v = _randn(gen, (num_pages, page_size, kv_heads, head_dim), dt, device)
+    k = _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, pool_layout)
+    v = _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, pool_layout)
     return Workload(name, q, k, v, sl.to(device), block_table=table.to(device),
-                    page_size=page_size, num_splits=num_splits, chunk_tokens=chunk_tokens)
+                    page_size=page_size, num_splits=num_splits, chunk_tokens=chunk_tokens,
+                    pool_layout=pool_layout)
 
 
 def redraw_kv(w: Workload, seed: int) -> Workload:
@@ -145,8 +164,13 @@ def redraw_kv(w: Workload, seed: int) -> Workload:
     that must not find one step's K/V in cache from the previous step."""
     gen = torch.Generator(device=w.k.device)
     gen.manual_seed(seed)
-    k = _randn(gen, tuple(w.k.shape), w.k.dtype, w.k.device, w.k_gain)
-    v = _randn(gen, tuple(w.v.shape), w.v.dtype, w.v.device)
+    if w.paged:
+        P, page, hkv, d = w.k.shape
+        k = _pool(gen, P, page, hkv, d, w.k.dtype, w.k.device, w.pool_layout, w.k_gain)
+        v = _pool(gen, P, page, hkv, d, w.v.dtype, w.v.device, w.pool_layout)
+    else:
+        k = _randn(gen, tuple(w.k.shape), w.k.dtype, w.k.device, w.k_gain)
+        v = _randn(gen, tuple(w.v.shape), w.v.dtype, w.v.device)
     return dataclasses.replace(w, k=k, v=v)
 
 
@@ -208,12 +232,15 @@ def mha_bf16_chunked(length: int = 65536, chunk: int = 1024, device="cpu") -> Wo
                       dtype="bf16", device=device, chunk_tokens=chunk, ws_format="olse")
 
 
-def paged_ragged_f16(batch: int = 16, lo: int = 1024, hi: int = 32768, device="cpu") -> Workload:
+def paged_ragged_f16(batch: int = 16, lo: int = 1024, hi: int = 32768, device="cpu",
+                     pool_layout: str = "hnd") -> Workload:
     """B=16, 32 query heads over 8 KV heads, D=128, lengths U[1024, 32768], fp16 pool of
-    16-token pages dealt out by a seeded permutation."""
+    16-token pages (head-major storage by default) dealt out by a seeded permutation."""
     lens = uniform_lengths(4, batch, lo, hi)
-    return paged(f"paged_gqa32x8_f16_B{batch}", seed=4, batch=batch, q_heads=32, kv_heads=8,
-                 head_dim=128, seq_lens=lens, page_size=16, dtype="f16", device=device)
+    suffix = "" if pool_layout == "hnd" else f"_{pool_layout}"
+    return paged(f"paged_gqa32x8_f16_B{batch}{suffix}", seed=4, batch=batch, q_heads=32, kv_heads=8,
+                 head_dim=128, seq_lens=lens, page_size=16, dtype="f16", device=device,
+                 pool_layout=pool_layout)
 
 
 def edge_gqa_f16(batch: int = 64, hi: int = 2048, device="cpu", forced_splits: int = 0,

@@ -101,6 +101,26 @@ typedef enum {
   FD_HEURISTIC_FA2 = 1
 } fd_heuristic;
 
+/* How split work is laid out over workgroups. */
+typedef enum {
+  /* BALANCED when the planner has host_seq_lens, the lengths differ, there
+   * are no more (sequence, KV head) segments than workgroup slots, no split
+   * count or chunk is forced, the MI355X rule is in use and the kernel
+   * supports it; else UNIFORM. */
+  FD_SCHEDULE_AUTO = 0,
+  /* One workgroup per (split, KV head, sequence); split s of every segment is
+   * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1). */
+  FD_SCHEDULE_UNIFORM = 1,
+  /* Needs host_seq_lens. The batch's (sequence, KV head) segments, each cut
+   * into granules of G tokens (G = the wave tile, or the page if larger), are
+   * laid end to end and cut into N near-equal ranges, one per workgroup
+   * (N = min(slots, cdiv(total granules, 4))). A segment crossing a range
+   * boundary yields one state per range; kanthi.in §6 asks for per-sequence
+   * split counts on ragged batches, and this is such a count, chosen so that
+   * every workgroup streams the same number of bytes. */
+  FD_SCHEDULE_BALANCED = 2
+} fd_schedule;
+
 /* Shape and layout of one decode step. All strides are in ELEMENTS. */
 typedef struct {
   int32_t batch;          /* B >= 1 */
@@ -143,7 +163,15 @@ typedef struct {
   int32_t heuristic;          /* fd_heuristic */
   int32_t max_splits;         /* 0: 128 */
   float overhead_budget;      /* 0: 0.02 (workspace bytes <= 2% of KV bytes) */
-  int32_t reserved[7];
+  int32_t num_host_seq_lens;  /* entries in host_seq_lens (0: none; else must equal batch) */
+  int32_t schedule;           /* fd_schedule */
+  int32_t reserved[5];
+  /* Optional HOST copy of seq_lens (int32 [batch]). With it the MI355X rule
+   * sizes splits from the batch's total work: no split longer than one
+   * slot's share, cdiv(Hkv * sum(len), slots) tokens, so a ragged batch is
+   * not bounded by its longest sequence. The kernels still read the device
+   * seq_lens; these must match them. */
+  const int32_t* host_seq_lens;
 } fd_plan_opts;
 
 /* A plan: caller-owned plain data, produced by fd_plan and read by the other
@@ -160,7 +188,9 @@ typedef struct {
   int32_t slots;              /* workgroup slots of one wave in the split rule */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (S, Hkv, B) */
   float scale;                /* resolved score scale */
-  int32_t reserved1;
+  int32_t schedule;           /* fd_schedule actually used (UNIFORM or BALANCED). BALANCED:
+                                 chunk_tokens is the granule G, grid (N, 1, 1), and S is the
+                                 largest number of pieces any (b, kv head) segment is cut into */
   int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
   int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
   int64_t ws_counter_bytes;   /* uint32 [B, Hkv] arrival counters of fd_decode_fused */

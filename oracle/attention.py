@@ -248,8 +248,10 @@ def decode_attention(cache: Cache, pairs: Optional[Iterable[Tuple[int, int]]] = 
 
 
 def split_states(cache: Cache, num_splits: int, chunk: int,
-                 pairs: Optional[Iterable[Tuple[int, int]]] = None):
-    """Per-split (m, ℓ, u) of every (b, hq) for the partition ``chunk_bounds``.
+                 pairs: Optional[Iterable[Tuple[int, int]]] = None, bounds=None):
+    """Per-split (m, ℓ, u) of every (b, hq) for the partition ``chunk_bounds``,
+    or, with ``bounds(b, hkv) -> [(lo, hi), ...]`` (at most S entries; missing
+    ones are empty splits), for that partition instead.
     Returns m [B, Hq, S], l [B, Hq, S], u [B, Hq, S, D] (NaN where not computed).
     m is the largest natural-log score of the split."""
     S = num_splits
@@ -259,7 +261,13 @@ def split_states(cache: Cache, num_splits: int, chunk: int,
     todo = pairs if pairs is not None else [(b, h) for b in range(cache.B) for h in range(cache.Hq)]
     for b, hq in todo:
         L = int(max(0, cache.seq_lens[b]))
-        for s, (lo, hi) in enumerate(chunk_bounds(L, chunk, S)):
+        if bounds is None:
+            parts = chunk_bounds(L, chunk, S)
+        else:
+            parts = list(bounds(b, cache.kv_head(hq)))
+            assert len(parts) <= S
+            parts += [(L, L)] * (S - len(parts))
+        for s, (lo, hi) in enumerate(parts):
             K, V = cache.rows(b, cache.kv_head(hq), lo, hi)
             M[b, hq, s], Lw[b, hq, s], U[b, hq, s] = segment_state(cache.q[b, hq], K, V, cache.scale)
     return M, Lw, U

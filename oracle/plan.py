@@ -89,3 +89,57 @@ def chunk_for(max_len: int, splits: int, align: int) -> int:
     boundaries to KV pages)."""
     c = max(1, cdiv(max(max_len, 1), splits))
     return cdiv(c, align) * align
+
+
+def chunk_from_lengths(lengths, max_len: int, kv_heads: int, slots: int, align: int, max_splits: int,
+                       group: int, head_dim: int, kv_elt: int, budget: float) -> int:
+    """Tokens per split for a batch whose lengths are known on the host: no
+    split longer than one slot's share of the total work, i.e. chunk =
+    cdiv(Hkv * sum(len), slots) rounded up to ``align``, then enlarged until
+    S = cdiv(max_len, chunk) respects ``max_splits`` and the workspace-traffic
+    budget of the §6 overhead check (kanthi.in). ``max_len`` is the problem's
+    bound on the lengths (the split grid spans it). With equal lengths this is
+    the split count at which the wave-efficiency rule fills one wave exactly.
+    Parity unpinned (derived from MI355X measurements)."""
+    if max_len <= 0:
+        return align
+    total = kv_heads * sum(max(0, int(x)) for x in lengths)
+    chunk = max(align, cdiv(cdiv(total, slots), align) * align)
+    while True:
+        s = cdiv(max_len, chunk)
+        if s <= max(1, max_splits) and (s == 1 or workspace_ratio(s, group, head_dim, kv_elt, max_len) <= budget):
+            return chunk
+        chunk += align
+
+
+def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_granules: int = 4):
+    """The balanced split schedule, from its definition: segment (b, h) is
+    cdiv(len_b, G) granules; the segments, in (b, h) order, form one line of T
+    granules; N = min(slots, cdiv(T, min_granules)) workgroups (1 if T = 0)
+    take the ranges [floor(w T / N), floor((w + 1) T / N)). Every non-empty
+    intersection of a range with a segment is one piece. Returns
+    (N, S, pieces) with pieces[(b, h)] = [(w, token_lo, token_hi), ...] in
+    workgroup order and S = the largest number of pieces of one segment (at
+    least 1). Variable-length batches want per-sequence split counts (kanthi.in
+    §6); this is one such count that gives every workgroup the same bytes.
+    Parity unpinned as a performance choice; its partition is checked
+    exhaustively in tests."""
+    lens = [max(0, int(n)) for n in lengths]
+    plens = [cdiv(n, granule) for n in lens]
+    T = kv_heads * sum(plens)
+    N = min(slots, cdiv(T, min_granules)) if T > 0 else 1
+    ranges = [(w * T // N, (w + 1) * T // N) for w in range(N)]
+    pieces = {}
+    x = 0
+    for b, (n, plen) in enumerate(zip(lens, plens)):
+        for h in range(kv_heads):
+            ss, se = x + h * plen, x + (h + 1) * plen
+            lst = []
+            for w, (gs, ge) in enumerate(ranges):
+                lo, hi = max(ss, gs), min(se, ge)
+                if lo < hi:
+                    lst.append((w, (lo - ss) * granule, min((hi - ss) * granule, n)))
+            pieces[(b, h)] = lst
+        x += kv_heads * plen
+    S = max([1] + [len(v) for v in pieces.values()])
+    return N, S, pieces

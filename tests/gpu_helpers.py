@@ -28,11 +28,15 @@ def say(*a):
 
 
 def plan_opts_for(w, **over):
+    """The plan options the benchmark uses: forced splits/chunk where the workload
+    fixes them, else the length-aware planner fed the host copy of the lengths."""
     opts = {"ws_format": w.ws_format}
     if w.num_splits:
         opts["force_splits"] = w.num_splits
     if w.chunk_tokens:
         opts["force_chunk_tokens"] = w.chunk_tokens
+    if not w.num_splits and not w.chunk_tokens:
+        opts["host_seq_lens"] = w.seq_lens.cpu().tolist()
     opts.update(over)
     return opts
 
@@ -44,7 +48,7 @@ def run(w, stream=None, **over):
     sl = w.seq_lens.to(dev)
     bt = None if w.block_table is None else w.block_table.to(dev)
     opts = plan_opts_for(w, **over)
-    say(f"run {w.name} opts={opts}")
+    say(f"run {w.name} opts={ {k_: v_ for k_, v_ in opts.items() if k_ != 'host_seq_lens'} }")
     prob = fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale)
     plan = fd.fd_plan(prob, **opts)
     ws_o, ws_stats = fd.workspace(plan, dev)
@@ -53,8 +57,26 @@ def run(w, stream=None, **over):
     fd.fd_decode_split(plan, q, k, v, sl, ws_o, ws_stats, bt, stream)
     fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
     torch.cuda.synchronize()
-    say(f"done {w.name} S={plan.num_splits} chunk={plan.chunk_tokens} kernel={plan.kernel}")
+    say(f"done {w.name} S={plan.num_splits} chunk={plan.chunk_tokens} kernel={plan.kernel} "
+        f"schedule={plan.schedule} grid={plan.grid_x}")
     return plan, out.cpu(), lse.cpu(), ws_o.cpu(), ws_stats.cpu()
+
+
+def run_fused(w, ctr=None, **over):
+    """Plan + fused split/merge on cuda:0. Returns (plan, out, lse, counters)."""
+    dev = torch.device("cuda", 0)
+    q, k, v, sl = w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev)
+    bt = None if w.block_table is None else w.block_table.to(dev)
+    opts = plan_opts_for(w, **over)
+    say(f"fused {w.name} opts={ {k_: v_ for k_, v_ in opts.items() if k_ != 'host_seq_lens'} }")
+    plan = fd.fd_plan(fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale), **opts)
+    ws_o, ws_stats = fd.workspace(plan, dev)
+    ctr = fd.counters(plan, dev) if ctr is None else ctr
+    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse, bt)
+    torch.cuda.synchronize()
+    return plan, out.cpu(), lse.cpu(), ctr
 
 
 def cache_of(w) -> A.Cache:

@@ -5,6 +5,8 @@ import math
 import os
 import re
 
+import numpy as np
+
 import pytest
 import torch
 
@@ -122,6 +124,88 @@ def test_mi355x_choices_for_the_workloads():
     assert p.chunk_tokens == 4000 and p.slots == 256
     assert fd.fd_plan(contiguous_problem(B=64, Hq=32, Hkv=8, L=2048), num_cus=256).num_splits == 1
     assert fd.fd_plan(contiguous_problem(Hq=32, Hkv=32, L=65536, dtype=2), num_cus=256).num_splits == 8
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_length_aware_rule_matches_oracle(paged):
+    """With host lengths the MI355X planner caps a split at one slot's share of
+    the batch's total work (oracle.plan.chunk_from_lengths)."""
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        B = int(rng.choice([1, 2, 3, 16, 64]))
+        Hkv, g = ((8, 8), (8, 4), (2, 2), (32, 1))[trial % 4]
+        kernel = "valu" if g == 1 else "auto"
+        hi = int(rng.choice([1, 40, 1000, 32768, 131072]))
+        lens = rng.integers(0, hi + 1, size=B)
+        L = max(int(lens.max()), 1) + int(rng.integers(0, 64))
+        mk = paged_problem if paged else contiguous_problem
+        prob = mk(B=B, Hq=Hkv * g, Hkv=Hkv, L=L)
+        plan = fd.fd_plan(prob, num_cus=256, kernel=kernel, host_seq_lens=lens.tolist(), schedule="uniform")
+        align = max(plan.tile_tokens, 16 if paged else 1)
+        chunk = OP.chunk_from_lengths(lens.tolist(), L, Hkv, 256, align, 128, g, 128, 2, 0.02)
+        assert plan.chunk_tokens == chunk, (B, Hkv, g, L, lens.tolist()[:4])
+        assert plan.num_splits == math.ceil(L / chunk)
+
+
+def test_length_aware_choices():
+    """Equal lengths reproduce the wave-filling choice; a ragged batch splits by
+    its total work, not by its longest row."""
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, host_seq_lens=[128000],
+                   schedule="uniform")
+    assert (p.num_splits, p.chunk_tokens) == (32, 4000)
+    lens = [32768] + [1024] * 15
+    p = fd.fd_plan(paged_problem(B=16, L=32768), num_cus=256, host_seq_lens=lens, schedule="uniform")
+    assert p.chunk_tokens == OP.cdiv(OP.cdiv(8 * sum(lens), 256), 32) * 32
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(paged_problem(B=16, L=32768), num_cus=256, host_seq_lens=lens[:15])
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(paged_problem(B=16, L=1000), num_cus=256, host_seq_lens=lens)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_schedule_matches_oracle(paged):
+    """Grid size, granule and slot count of the balanced plan equal the
+    oracle's schedule from its definition."""
+    rng = np.random.default_rng(29)
+    for trial in range(80):
+        B = int(rng.choice([1, 2, 5, 16, 64]))
+        Hkv, g = ((8, 8), (8, 4), (2, 2), (4, 2))[trial % 4]
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(0, int(rng.choice([40, 2048, 40000])), B)]
+        L = max(lens + [1])
+        cus = int(rng.choice([7, 64, 256]))
+        mk = paged_problem if paged else contiguous_problem
+        page = int(rng.choice([16, 64])) if paged else 0
+        prob = mk(B=B, Hq=Hkv * g, Hkv=Hkv, L=L, **({"page": page} if paged else {}))
+        plan = fd.fd_plan(prob, num_cus=cus, host_seq_lens=lens, schedule="balanced")
+        assert plan.schedule == fd.SCHEDULES["balanced"]
+        G = max(32, page)
+        N, S, _ = OP.balanced_schedule(lens, Hkv, G, cus)
+        assert (plan.grid_x, plan.grid_y, plan.grid_z) == (N, 1, 1), (lens, cus)
+        assert plan.num_splits == S and plan.chunk_tokens == G
+        assert plan.ws_o_bytes == B * Hkv * g * S * 128 * 4
+
+
+def test_schedule_selection():
+    lens = [3000, 10, 0]
+    prob = contiguous_problem(B=3, Hq=32, Hkv=8, L=3000)
+    assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens).schedule == fd.SCHEDULES["balanced"]
+    assert fd.fd_plan(prob, num_cus=256).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, schedule="uniform").schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, force_splits=4).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, heuristic="fa2").schedule == fd.SCHEDULES["uniform"]
+    # equal lengths, or more segments than slots: uniform
+    assert fd.fd_plan(prob, num_cus=256, host_seq_lens=[3000] * 3).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens, schedule="balanced").schedule == fd.SCHEDULES["balanced"]
+    # the VALU kernel has no balanced variant: AUTO falls back, an explicit request fails
+    mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=3000)
+    assert fd.fd_plan(mha, num_cus=256, host_seq_lens=lens).schedule == fd.SCHEDULES["uniform"]
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, schedule="balanced")
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(prob, num_cus=256, schedule="balanced")            # needs host lengths
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, schedule="balanced", force_splits=2)
 
 
 def test_forced_splits_and_chunk():

@@ -63,11 +63,13 @@ def test_paged_ragged_f16():
     H.check_against_oracle(w, out, lse, pairs)
 
 
-def test_edge_gqa_plan_splits():
+@pytest.mark.parametrize("schedule", ["auto", "uniform"])
+def test_edge_gqa_plan_splits(schedule):
     w = W.edge_gqa_f16()
-    plan, out, lse, _, _ = H.run(w)
-    H.say(f"edge plan: S={plan.num_splits}")
-    assert plan.num_splits == 1                         # 512 work units fill the machine
+    plan, out, lse, _, _ = H.run(w, schedule=schedule)
+    H.say(f"edge plan: S={plan.num_splits} schedule={plan.schedule}")
+    if schedule == "uniform":
+        assert plan.num_splits == 1                     # 512 work units fill the machine
     H.check_against_oracle(w, out, lse)                 # every (b, hq)
 
 

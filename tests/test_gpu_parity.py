@@ -120,15 +120,35 @@ def test_zero_length_rows():
 # Paged layout
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("layout", ["hnd", "nhd"])
 @pytest.mark.parametrize("page", [16, 32, 64])
 @pytest.mark.parametrize("g", [1, 4])
-def test_paged_small(page, g):
+def test_paged_small(page, g, layout):
     lens = [1000, 17, 333, 16]
-    w = W.paged(f"paged_p{page}_g{g}", seed=50 + page, batch=4, q_heads=4 * g, kv_heads=4, head_dim=128,
-                seq_lens=lens, page_size=page, dtype="f16", extra_pages=3)
+    w = W.paged(f"paged_p{page}_g{g}_{layout}", seed=50 + page, batch=4, q_heads=4 * g, kv_heads=4,
+                head_dim=128, seq_lens=lens, page_size=page, dtype="f16", extra_pages=3, pool_layout=layout)
     for splits in (1, 3):
         plan, out, lse, _, _ = H.run(w, force_splits=splits)
         H.check_against_oracle(w, out, lse)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_length_aware_plan(paged):
+    """A ragged batch planned from its host lengths (splits sized by total work)
+    and without them (by the longest row): both match the oracle."""
+    lens = [3000, 40, 1, 0, 2500, 700]
+    if paged:
+        w = W.paged("lenaware_paged", seed=56, batch=6, q_heads=16, kv_heads=2, head_dim=128, seq_lens=lens,
+                    page_size=16, dtype="f16")
+    else:
+        w = W.contiguous("lenaware", seed=57, batch=6, q_heads=16, kv_heads=2, head_dim=128, capacity=3000,
+                         seq_lens=lens, dtype="bf16")
+    seen = set()
+    for opts in ({"host_seq_lens": lens}, {"host_seq_lens": None}, {"host_seq_lens": lens, "num_cus": 7}):
+        plan, out, lse, _, _ = H.run(w, **opts)
+        seen.add(plan.num_splits)
+        H.check_against_oracle(w, out, lse)
+    assert len(seen) >= 2, seen
 
 
 # ---------------------------------------------------------------------------
@@ -258,20 +278,7 @@ def test_occupancy_table_matches_device():
 # Fused merge (one launch): last workgroup per (sequence, KV head) merges
 # ---------------------------------------------------------------------------
 
-def _run_fused(w, ctr=None, **over):
-    dev = torch.device("cuda", 0)
-    q, k, v, sl = w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev)
-    bt = None if w.block_table is None else w.block_table.to(dev)
-    opts = H.plan_opts_for(w, **over)
-    H.say(f"fused {w.name} opts={opts}")
-    plan = fd.fd_plan(fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale), **opts)
-    ws_o, ws_stats = fd.workspace(plan, dev)
-    ctr = fd.counters(plan, dev) if ctr is None else ctr
-    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=dev)
-    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
-    fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse, bt)
-    torch.cuda.synchronize()
-    return plan, out.cpu(), lse.cpu(), ctr
+_run_fused = H.run_fused
 
 
 @pytest.mark.parametrize("case", ["gqa_f16", "mha_bf16_valu", "paged", "tiny_f32", "zero_rows"])

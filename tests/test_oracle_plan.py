@@ -57,3 +57,36 @@ def test_chunk_for():
     assert P.chunk_for(1000, 3, 1) == 334
     assert P.chunk_for(128000, 56, 128) == 2304
     assert P.chunk_for(0, 4, 16) == 16
+
+
+def test_balanced_schedule_partitions_every_segment():
+    """Pieces tile each segment exactly, in order; every workgroup's share of
+    the line differs from the others' by at most one granule; a workgroup
+    meets a segment at most once; zero-length rows get no pieces."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        B = int(rng.integers(1, 12))
+        hkv = int(rng.choice([1, 2, 8]))
+        G = int(rng.choice([16, 32, 64]))
+        lens = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(0, int(rng.choice([5, 300, 5000])), B)]
+        slots = int(rng.choice([1, 3, 7, 64, 256]))
+        N, S, pieces = P.balanced_schedule(lens, hkv, G, slots)
+        T = hkv * sum(-(-n // G) for n in lens)
+        assert 1 <= N <= max(1, min(slots, T))
+        share = [0] * N
+        for (b, h), lst in pieces.items():
+            n = lens[b]
+            assert len(lst) <= S
+            if n == 0:
+                assert lst == []
+                continue
+            assert lst[0][1] == 0 and lst[-1][2] == n
+            for (w0, _, hi0), (w1, lo1, _) in zip(lst, lst[1:]):
+                assert hi0 == lo1 and w1 == w0 + 1 and lo1 % G == 0
+            for w, lo, hi in lst:
+                assert lo < hi
+                share[w] += -(-hi // G) - lo // G
+        assert sum(share) == T
+        if T:
+            assert max(share) - min(share) <= 1
