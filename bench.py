@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = planner)")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate (0 = enough for 2x the MALL)")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
-    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+    ap.add_argument("--path", choices=["fused", "split"], default="split",
                     help="fused: one launch (last workgroup per group merges); split: split + merge kernels")
     ap.add_argument("--schedule", choices=["auto", "uniform", "balanced"], default="auto",
                     help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
