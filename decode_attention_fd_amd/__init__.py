@@ -106,6 +106,9 @@ def lib() -> ctypes.CDLL:
         L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge.restype = ctypes.c_int
+        L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.fd_merge_states.restype = ctypes.c_int
         L.fd_status_str.argtypes = [ctypes.c_int]
         L.fd_status_str.restype = ctypes.c_char_p
         L.fd_last_hip_error.argtypes = []
@@ -257,6 +260,37 @@ def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:
     st = lib().fd_merge(ctypes.byref(plan), _ptr(ws_o), _ptr(ws_stats), _ptr(out), _ptr(lse),
                         _stream_handle(stream))
     _check(st, "fd_merge")
+
+
+def fd_merge_states(states, stats, out=None, lse_out=None, *, ws_format: str = "olse", stream=None):
+    """Merge external attention states per row (the library's merge operator on
+    caller-built states). states float32 [..., S, D]; stats float32 [..., S]
+    (olse: natural-log LSE) or [..., S, 2] (uml: m, l). Returns (out [..., D],
+    lse_out [...]), allocating them when not given."""
+    fmt = WS_FORMATS[ws_format]
+    if states.dtype != torch.float32 or stats.dtype != torch.float32:
+        raise ValueError("states and stats must be float32")
+    if not states.is_contiguous() or not stats.is_contiguous():
+        raise ValueError("states and stats must be contiguous")
+    *lead, S, D = states.shape
+    want = (*lead, S, 2) if fmt == WS_FORMATS["uml"] else (*lead, S)
+    if tuple(stats.shape) != tuple(want):
+        raise ValueError(f"stats shape {tuple(stats.shape)} != {tuple(want)}")
+    rows = 1
+    for n in lead:
+        rows *= n
+    if out is None:
+        out = torch.empty(*lead, D, dtype=torch.float32, device=states.device)
+    if lse_out is None:
+        lse_out = torch.empty(*lead, dtype=torch.float32, device=states.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != rows * D:
+        raise ValueError("out must be a contiguous float32 tensor of rows x D")
+    if lse_out.dtype != torch.float32 or not lse_out.is_contiguous() or lse_out.numel() != rows:
+        raise ValueError("lse_out must be a contiguous float32 tensor of rows")
+    st = lib().fd_merge_states(fmt, _ptr(states), _ptr(stats), rows, S, D, _ptr(out), _ptr(lse_out),
+                               _stream_handle(stream))
+    _check(st, "fd_merge_states")
+    return out, lse_out
 
 
 def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,

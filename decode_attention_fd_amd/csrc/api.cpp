@@ -262,4 +262,27 @@ FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_st
   return FD_OK;
 }
 
+FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,
+                           int32_t num_states, int32_t head_dim, float* out, float* lse_out, void* stream) {
+  if (ws_format != FD_WS_UML && ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
+  if (rows < 0 || rows > 0x7fffffff || num_states < 1 || num_states > 65535) return FD_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
+  if (rows == 0) return FD_OK;
+  if (!states || !stats || !out) return FD_ERR_INVALID_ARG;
+  if (!aligned(states, 16) || !aligned(stats, ws_format == FD_WS_UML ? 8 : 4) || !aligned(out, 16) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return FD_ERR_ALIGNMENT;
+  MergeParams p;
+  p.ws_o = states;
+  p.ws_stats = stats;
+  p.out = out;
+  p.lse = lse_out;
+  p.BH = (int32_t)rows;
+  p.S = num_states;
+  p.ws_format = ws_format;
+  int err = launch_merge(p, head_dim, stream);
+  if (err) return hip_fail(err, "merge kernel launch");
+  return FD_OK;
+}
+
 }  // extern "C"

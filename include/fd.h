@@ -244,6 +244,27 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
                            float* ws_stats, size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes,
                            float* out, float* lse, void* stream);
 
+/* Merge externally produced attention states, one output per row: the ⊕
+ * operator of kanthi.in §2 (stable form) exposed on its own, for cascade
+ * attention over shared prefixes and for states gathered from other devices
+ * (§7 "across GPUs"); FlashInfer's merge_state does the same on its page
+ * "FlashInfer Attention States".
+ *   ws_format FD_WS_OLSE: states[r, s, :] is a normalised output o_s and
+ *     stats[r, s] its natural-log LSE; O = sum_s w_s o_s / sum_s w_s with
+ *     w_s = e^{lse_s - max lse}, LSE = max + ln(sum_s w_s).
+ *   ws_format FD_WS_UML: states[r, s, :] is u_s = sum_i e^{x_i - m_s} v_i,
+ *     stats[r, s, 0:2] = (m_s, l_s) in natural log; O = sum w_s u_s / sum w_s
+ *     l_s with w_s = e^{m_s - max m}, LSE = max + ln(sum w_s l_s).
+ * A state with lse (m) = -inf weighs 0; a row whose states are all -inf gets
+ * O = 0 and LSE = -inf. Layouts (float32, contiguous, device memory):
+ * states [rows, num_states, head_dim], stats [rows, num_states] (OLSE) or
+ * [rows, num_states, 2] (UML), out [rows, head_dim], lse_out [rows] or NULL.
+ * head_dim in {64, 128}; 1 <= num_states <= 65535; 0 <= rows <= 2^31 - 1
+ * (rows = 0 launches nothing). Inputs are read only; the caller owns every
+ * buffer. Arguments are checked on the host before any launch. */
+FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,
+                           int32_t num_states, int32_t head_dim, float* out, float* lse_out, void* stream);
+
 /* Human-readable text for an fd_status. Never NULL. */
 FD_API const char* fd_status_str(int status);
 

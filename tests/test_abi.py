@@ -300,6 +300,36 @@ def test_decode_and_merge_validation_without_gpu():
     assert _split_status(paged, good) == fd.FD_ERR_INVALID_ARG          # no block table
 
 
+def test_merge_states_validation_without_gpu():
+    """Every argument error of fd_merge_states is caught on the host, before
+    any launch (so none of these calls touches a device)."""
+    L = fd.lib()
+    olse, uml = fd.WS_FORMATS["olse"], fd.WS_FORMATS["uml"]
+    ok = (0x10000, 0x20000, 8, 4, 128, 0x30000, 0x40000, None)
+
+    def st(fmt, *a):
+        return L.fd_merge_states(fmt, *a)
+    assert st(7, *ok) == fd.FD_ERR_INVALID_ARG                             # format
+    assert st(olse, 0x10000, 0x20000, -1, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, 1 << 31, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, 8, 0, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, 8, 65536, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, 8, 4, 96, 0x30000, None, None) == fd.FD_ERR_UNSUPPORTED
+    assert st(olse, None, 0x20000, 8, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, None, 8, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, 8, 4, 128, None, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10004, 0x20000, 8, 4, 128, 0x30000, None, None) == fd.FD_ERR_ALIGNMENT
+    assert st(olse, 0x10000, 0x20002, 8, 4, 128, 0x30000, None, None) == fd.FD_ERR_ALIGNMENT
+    assert st(uml, 0x10000, 0x20004, 8, 4, 128, 0x30000, None, None) == fd.FD_ERR_ALIGNMENT
+    assert st(olse, 0x10000, 0x20000, 8, 4, 128, 0x30008, None, None) == fd.FD_ERR_ALIGNMENT
+    assert st(olse, 0x10000, 0x20000, 8, 4, 128, 0x30000, 0x40002, None) == fd.FD_ERR_ALIGNMENT
+    assert st(olse, None, None, 0, 4, 128, None, None, None) == fd.FD_OK  # zero rows: nothing to do
+    with pytest.raises(ValueError):
+        fd.fd_merge_states(torch.zeros(3, 4, 128), torch.zeros(3, 5))
+    with pytest.raises(ValueError):
+        fd.fd_merge_states(torch.zeros(3, 4, 128), torch.zeros(3, 4), ws_format="uml")
+
+
 def test_problem_for_tensors():
     q = torch.zeros(2, 16, 128, dtype=torch.float16)
     k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)
