@@ -29,6 +29,11 @@ Readings where the pages are silent (each is listed in the design doc):
 * Paged pools are ``[num_pages, page_size, Hkv, D]`` and token t of sequence
   b is row ``t % page_size`` of page ``block_table[b, t // page_size]``
   ([KANTHI] §7 and §9 name a pool plus block table but no layout).
+* A short query block (speculative decode, [KANTHI] §7 "Short query blocks"
+  and §9 item 1: q is [B, q_len, Hq, D]) holds the last q_len positions of
+  the sequence, whose keys are already in the cache; row i sees the first
+  seq_len − (q_len − 1 − i) tokens ([XUUJII] §06: every query keeps its own
+  visibility). Rows that see no token follow the empty-row convention.
 
 Every stored input (fp16, bf16 or fp32) is upcast exactly to float64; all
 arithmetic below is float64.
@@ -57,6 +62,8 @@ def f64(x) -> np.ndarray:
 
 
 def ints(x) -> np.ndarray:
+    if isinstance(x, (list, tuple)):
+        return np.asarray(x, dtype=np.int64)
     if isinstance(x, np.ndarray):
         return x.astype(np.int64)
     return x.detach().to("cpu").to(dtype=__import__("torch").int64).numpy()
@@ -244,6 +251,31 @@ def decode_attention(cache: Cache, pairs: Optional[Iterable[Tuple[int, int]]] = 
     todo = pairs if pairs is not None else [(b, h) for b in range(cache.B) for h in range(cache.Hq)]
     for b, hq in todo:
         O[b, hq], LSE[b, hq] = attention_one(cache, b, hq)
+    return O, LSE
+
+
+def block_row_cache(q_block, k, v, seq_lens, i: int, block_table=None, scale: Optional[float] = None) -> Cache:
+    """Row i of a short query block as a single-query decode step: query
+    q_block[:, i] over the first seq_len − (q_len − 1 − i) tokens (clamped at 0)."""
+    q_len = q_block.shape[1]
+    lens = ints(seq_lens) - (q_len - 1 - i)
+    return Cache(q_block[:, i], k, v, np.maximum(lens, 0), block_table, scale)
+
+
+def decode_attention_block(q_block, k, v, seq_lens, block_table=None, scale: Optional[float] = None,
+                           rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """O [B, q_len, Hq, D] and LSE [B, q_len, Hq] of a short query block, by the
+    definition: each (b, i, hq) attends to its visible prefix. With ``rows``
+    only those (b, i, hq) are computed and the rest are NaN."""
+    B, q_len, Hq, D = q_block.shape
+    O = np.full((B, q_len, Hq, D), np.nan)
+    LSE = np.full((B, q_len, Hq), np.nan)
+    want = None if rows is None else sorted(set(rows))
+    for i in range(q_len):
+        pairs = None if want is None else [(b, h) for b, ii, h in want if ii == i]
+        if pairs == []:
+            continue
+        O[:, i], LSE[:, i] = decode_attention(block_row_cache(q_block, k, v, seq_lens, i, block_table, scale), pairs)
     return O, LSE
 
 

@@ -446,3 +446,59 @@ def test_planted_mistakes_are_caught(monkeypatch, name, fn):
     monkeypatch.setattr(A, name, fn)
     with pytest.raises(AssertionError):
         _all_pins()
+
+
+# ---------------------------------------------------------------------------
+# Short query blocks (speculative decode)
+# ---------------------------------------------------------------------------
+
+def _masked_softmax_block(q, K, V, L, scale):
+    """Brute force, written independently: scores of every (row i, token t) for
+    t < L, with the bottom-right causal mask t > L - q_len + i set to -inf."""
+    q_len = q.shape[0]
+    s = (q @ K[:L].T) * scale
+    t = np.arange(L)[None, :]
+    i = np.arange(q_len)[:, None]
+    s = np.where(t > L - q_len + i, -np.inf, s)
+    out = np.zeros((q_len, V.shape[1]))
+    lse = np.full(q_len, -np.inf)
+    for r in range(q_len):
+        if np.all(np.isneginf(s[r])):
+            continue
+        m = s[r].max()
+        e = np.exp(s[r] - m)
+        out[r] = e @ V[:L] / e.sum()
+        lse[r] = m + np.log(e.sum())
+    return out, lse
+
+
+def test_block_rows_against_brute_force():
+    rng = np.random.default_rng(11)
+    for q_len in (1, 2, 4, 8):
+        for L in (0, 1, 3, q_len, q_len + 1, 40):
+            B, Hq, Hkv, D = 2, 4, 2, 8
+            q = rng.standard_normal((B, q_len, Hq, D))
+            k = rng.standard_normal((B, Hkv, 48, D))
+            v = rng.standard_normal((B, Hkv, 48, D))
+            lens = np.array([L, max(0, L - 1)])
+            O, LSE = A.decode_attention_block(q, k, v, lens, scale=0.5)
+            for b in range(B):
+                for h in range(Hq):
+                    ro, rl = _masked_softmax_block(q[b, :, h], k[b, h // 2], v[b, h // 2], int(lens[b]), 0.5)
+                    assert np.allclose(O[b, :, h], ro, atol=1e-12)
+                    assert np.array_equal(np.isneginf(LSE[b, :, h]), np.isneginf(rl))
+                    fin = np.isfinite(rl)
+                    assert np.allclose(LSE[b, fin, h], rl[fin], atol=1e-12)
+
+
+def test_block_last_row_is_single_query_decode():
+    """The last row of a block sees the whole cache: it equals single-query
+    decode over seq_len; row i equals it over seq_len - (q_len - 1 - i)."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 4, 2, 16))
+    k = rng.standard_normal((1, 2, 30, 16))
+    v = rng.standard_normal((1, 2, 30, 16))
+    O, LSE = A.decode_attention_block(q, k, v, [30])
+    for i in range(4):
+        o1, l1 = A.decode_attention(A.Cache(q[:, i], k, v, [30 - (3 - i)]))
+        assert np.array_equal(O[:, i], o1) and np.array_equal(LSE[:, i], l1)
