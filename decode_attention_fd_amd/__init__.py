@@ -44,7 +44,7 @@ class Problem(ctypes.Structure):
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("bt_stride_b", ctypes.c_int64),
         ("pool_stride_page", ctypes.c_int64), ("pool_stride_t", ctypes.c_int64), ("pool_stride_h", ctypes.c_int64),
-        ("scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("q_len", ctypes.c_int32), ("q_stride_q", ctypes.c_int64),
     ]
 
 
@@ -152,19 +152,25 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: tor
                 scale: float = 0.0) -> Problem:
     """Describe a decode step from its tensors (shapes and strides only).
 
-    q [B, Hq, D]; contiguous K/V [B, Hkv, T, D] or paged pools [P, page, Hkv, D]
-    with ``block_table`` int32 [B, max_pages]. ``max_seq_len`` defaults to
-    ``seq_lens.max()`` (a device sync if seq_lens lives on the GPU)."""
+    q [B, Hq, D], or [B, q_len, Hq, D] for a short query block (row i of the
+    block sees the first seq_len - (q_len - 1 - i) tokens); contiguous K/V
+    [B, Hkv, T, D] or paged pools [P, page, Hkv, D] with ``block_table`` int32
+    [B, max_pages]. ``max_seq_len`` defaults to ``seq_lens.max()`` (a device
+    sync if seq_lens lives on the GPU)."""
     if k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("K and V must have the same shape and strides")
     if k.dtype not in DTYPES or q.dtype not in DTYPES:
         raise ValueError(f"unsupported dtype {k.dtype}/{q.dtype}")
     p = Problem()
-    p.batch, p.num_q_heads, p.head_dim = q.shape
+    if q.dim() == 4:
+        p.batch, p.q_len, p.num_q_heads, p.head_dim = q.shape
+        p.q_stride_b, p.q_stride_q, p.q_stride_h = q.stride(0), q.stride(1), q.stride(2)
+    else:
+        p.batch, p.num_q_heads, p.head_dim = q.shape
+        p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
     p.q_dtype = DTYPES[q.dtype]
     p.kv_dtype = DTYPES[k.dtype]
-    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
-    if q.stride(2) != 1 or k.stride(3) != 1:
+    if q.stride(-1) != 1 or k.stride(3) != 1:
         raise ValueError("the head dimension must be contiguous")
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
@@ -215,12 +221,13 @@ def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_sp
 
 
 def workspace(plan: Plan, device) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Allocate the fp32 workspace the plan asks for: (ws_o [B,Hq,S,D], ws_stats)."""
+    """Allocate the fp32 workspace the plan asks for: (ws_o [B,(q_len,)Hq,S,D], ws_stats)."""
     pr = plan.prob
     S, D = plan.num_splits, pr.head_dim
-    ws_o = torch.empty(pr.batch, pr.num_q_heads, S, D, dtype=torch.float32, device=device)
+    rows = (pr.batch, pr.q_len, pr.num_q_heads) if pr.q_len > 1 else (pr.batch, pr.num_q_heads)
+    ws_o = torch.empty(*rows, S, D, dtype=torch.float32, device=device)
     last = 2 if plan.ws_format == WS_FORMATS["uml"] else 1
-    ws_stats = torch.empty(pr.batch, pr.num_q_heads, S, last, dtype=torch.float32, device=device)
+    ws_stats = torch.empty(*rows, S, last, dtype=torch.float32, device=device)
     return ws_o, ws_stats
 
 
@@ -299,8 +306,8 @@ def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale
     (out, lse) fp32 (lse None if not asked)."""
     plan = fd_plan(problem_for(q, k, v, seq_lens, block_table, max_seq_len, scale), **plan_options)
     ws_o, ws_stats = workspace(plan, q.device)
-    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=q.device)
-    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device) if return_lse else None
+    out = torch.empty(*q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=q.device) if return_lse else None
     if fused:
         fd_decode_fused(plan, q, k, v, seq_lens, ws_o, ws_stats, counters(plan, q.device), out, lse, block_table,
                         stream)

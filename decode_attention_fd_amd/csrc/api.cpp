@@ -119,7 +119,7 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   if (st != FD_OK) return st;
   const int kernel = choose_kernel(prob, o.kernel);
   if (kernel < 0) return -kernel;
-  const int gtpl = valu_group_template(prob->num_q_heads / prob->num_kv_heads);
+  const int gtpl = valu_group_template(prob->num_q_heads / prob->num_kv_heads * (prob->q_len > 1 ? prob->q_len : 1));
   // Resident split workgroups per CU: the device's answer when we query it,
   // else the table generated from the compiler's resource usage.
   int resident = 0;
@@ -183,6 +183,9 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
   p.Hq = pr.num_q_heads;
   p.Hkv = pr.num_kv_heads;
   p.g = plan->group;
+  p.q_len = pr.q_len > 1 ? pr.q_len : 1;
+  p.q_sq = pr.q_stride_q;
+  p.R = p.g * p.q_len;
   p.S = plan->num_splits;
   p.chunk = plan->chunk_tokens;
   if (paged) {
@@ -211,7 +214,7 @@ int launch_split(const fd_plan_t* plan, const SplitParams& p, void* stream) {
   if (plan->kernel == FD_KERNEL_MFMA)
     err = launch_split_mfma(p, pr.head_dim, pr.kv_dtype, pr.layout, stream);
   else
-    err = launch_split_valu(p, pr.head_dim, pr.kv_dtype, pr.layout, valu_group_template(plan->group), stream);
+    err = launch_split_valu(p, pr.head_dim, pr.kv_dtype, pr.layout, valu_group_template(p.R), stream);
   if (err) return hip_fail(err, "split kernel launch");
   return FD_OK;
 }
@@ -254,7 +257,7 @@ FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_st
   p.ws_stats = ws_stats;
   p.out = out;
   p.lse = lse;
-  p.BH = plan->prob.batch * plan->prob.num_q_heads;
+  p.BH = plan->prob.batch * (plan->prob.q_len > 1 ? plan->prob.q_len : 1) * plan->prob.num_q_heads;
   p.S = plan->num_splits;
   p.ws_format = plan->ws_format;
   int err = launch_merge(p, plan->prob.head_dim, stream);

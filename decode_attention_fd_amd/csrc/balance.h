@@ -31,7 +31,7 @@
 namespace fd {
 
 // Neutral state (u = 0 or o = 0, m = -inf or lse = -inf, l = 0) in split slots
-// [s0, s1) of the g rows of group (b, kvh).
+// [s0, s1) of the g * q_len state rows of group (b, kvh).
 template <int D, int NTHREADS>
 __device__ __forceinline__ void write_neutral(const SplitParams& p, int b, int kvh, int s0, int s1) {
   const int n = s1 - s0;
@@ -39,12 +39,12 @@ __device__ __forceinline__ void write_neutral(const SplitParams& p, int b, int k
   const bool co = p.fused != 0;
   const bool uml = p.ws_format == FD_WS_UML;
   const int per_row = n * D;
-  for (int i = threadIdx.x; i < p.g * per_row; i += NTHREADS) {
+  for (int i = threadIdx.x; i < p.R * per_row; i += NTHREADS) {
     const int h = i / per_row;
     const int r = i - h * per_row;
     const int s = s0 + r / D;
     const int d = r - (r / D) * D;
-    const int64_t base = ((int64_t)b * p.Hq + (int64_t)kvh * p.g + h) * p.S + s;
+    const int64_t base = state_row(p, b, kvh, h) * p.S + s;
     ws_store(p.ws_o + base * D + d, 0.f, co);
     if (d == 0) {
       if (uml) {
@@ -62,9 +62,10 @@ __device__ __forceinline__ void write_neutral(const SplitParams& p, int b, int k
 template <int D, int NTHREADS>
 __device__ __forceinline__ void empty_row(const SplitParams& p, int b) {
   if (p.fused) {
-    for (int i = threadIdx.x; i < p.Hq * D; i += NTHREADS) {
-      p.out[(int64_t)b * p.Hq * D + i] = 0.f;
-      if (p.lse && i % D == 0) p.lse[(int64_t)b * p.Hq + i / D] = -INFINITY;
+    const int rows = p.q_len * p.Hq;          // the row's query block, contiguous in out/lse
+    for (int i = threadIdx.x; i < rows * D; i += NTHREADS) {
+      p.out[(int64_t)b * rows * D + i] = 0.f;
+      if (p.lse && i % D == 0) p.lse[(int64_t)b * rows + i / D] = -INFINITY;
     }
   } else {
     for (int kvh = 0; kvh < p.Hkv; ++kvh) write_neutral<D, NTHREADS>(p, b, kvh, 0, p.S);
@@ -175,10 +176,10 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   return st;
 }
 
-// Walk this workgroup's range. piece(b, kvh, start, end, slot, count, last)
-// handles tokens [start, end) of segment (b, kvh): its state goes to `slot`,
-// the segment has `count` pieces in all, and `last` says that this workgroup
-// holds the segment's final granule. empty_row(b) handles a row of length 0
+// Walk this workgroup's range. piece(b, kvh, start, end, slot, count, last,
+// len) handles tokens [start, end) of segment (b, kvh) of a row of length
+// len: its state goes to `slot`, the segment has `count` pieces in all, and
+// `last` says that this workgroup holds the segment's final granule. empty_row(b) handles a row of length 0
 // whose position this workgroup owns.
 template <int NTHREADS, typename Piece, typename EmptyRow>
 __device__ __forceinline__ void balanced_walk(const SplitParams& p, Piece&& piece, EmptyRow&& empty_row) {
@@ -209,7 +210,7 @@ __device__ __forceinline__ void balanced_walk(const SplitParams& p, Piece&& piec
       const int slot = (int)(w - first);
       const int count = (int)(granule_owner(se - 1, st.total, nwg) - first + 1);
       const int64_t t1 = (pe - ss) * G;
-      piece(b, h, (int)((ps - ss) * G), (int)(t1 < len ? t1 : len), slot, count, se <= st.ge);
+      piece(b, h, (int)((ps - ss) * G), (int)(t1 < len ? t1 : len), slot, count, se <= st.ge, len);
     }
     x += p.Hkv * plen;
   }

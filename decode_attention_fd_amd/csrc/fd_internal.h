@@ -23,6 +23,9 @@ struct SplitParams {
   int64_t pool_sp, pool_st, pool_sh;    // paged
   int64_t bt_sb;
   int32_t B, Hq, Hkv, g;
+  int32_t q_len;                        // query rows per sequence (>= 1)
+  int64_t q_sq;                         // element stride between a sequence's query rows
+  int32_t R;                            // state rows per (sequence, KV head): g * q_len
   int32_t S, chunk;
   int32_t cap_tokens;                   // seq_lens are clamped to [0, cap_tokens]
   int32_t page_log2, num_pages;

@@ -90,6 +90,14 @@ namespace fd {
 // Stores of split states that another workgroup may read in the same launch
 // (fused merge) go out as agent-scope atomic stores: device-coherent
 // write-through stores, so publishing them needs no cache-wide write-back.
+// Output / workspace row of state row r (< g * q_len) of group (b, kvh): query
+// row i = r / g of the block, head kvh * g + r % g.
+__device__ __forceinline__ int64_t state_row(const SplitParams& p, int b, int kvh, int r) {
+  const int i = r / p.g;
+  const int h = r - i * p.g;
+  return ((int64_t)b * p.q_len + i) * p.Hq + (int64_t)kvh * p.g + h;
+}
+
 __device__ __forceinline__ void ws_store(float* p, float v, bool coherent) {
   if (coherent)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -153,7 +161,7 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   if (!s_last) return;
 
   constexpr int LPR = D / 4;
-  const int g = p.g;
+  const int g = p.R;                          // rows of the group
   const int SG = 1 << split_groups_log2(p.S, LPR, g, NTHREADS);
   const int tpr = LPR * SG;
   const int h = threadIdx.x / tpr;
@@ -162,7 +170,7 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   const int dl = t - grp * LPR;
   const bool active = h < g;
   const bool uml = p.ws_format == FD_WS_UML;
-  const int64_t row = (int64_t)b * p.Hq + (int64_t)kvh * g + h;
+  const int64_t row = state_row(p, b, kvh, active ? h : 0);
 
   RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
   if (active)

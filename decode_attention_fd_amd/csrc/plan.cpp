@@ -83,6 +83,11 @@ int validate_problem(const fd_problem* p) {
   const int64_t D = p->head_dim;
   if (p->q_stride_h < D || p->q_stride_b < 0) return FD_ERR_INVALID_ARG;
   if ((p->q_stride_h * elt) % 16 || (p->q_stride_b * elt) % 16) return FD_ERR_ALIGNMENT;
+  if (p->q_len < 0 || p->q_len > 8) return FD_ERR_UNSUPPORTED;
+  if (p->q_len > 1) {
+    if (p->q_stride_q < 0) return FD_ERR_INVALID_ARG;
+    if ((p->q_stride_q * elt) % 16) return FD_ERR_ALIGNMENT;
+  }
   if (p->layout == FD_LAYOUT_CONTIGUOUS) {
     if (p->kv_stride_t < D || p->kv_stride_h < 0 || p->kv_stride_b < 0) return FD_ERR_INVALID_ARG;
     if (p->kv_capacity < p->max_seq_len || p->kv_capacity < 0) return FD_ERR_INVALID_ARG;
@@ -108,7 +113,8 @@ int valu_group_template(int g) {
 }
 
 int choose_kernel(const fd_problem* p, int requested) {
-  const int g = p->num_q_heads / p->num_kv_heads;
+  // g = query rows one KV head serves: the group's heads times the block's queries.
+  const int g = p->num_q_heads / p->num_kv_heads * (p->q_len > 1 ? p->q_len : 1);
   const bool half = dtype_size(p->kv_dtype) == 2;
   const bool mfma_ok = half && g <= 8;
   const bool valu_ok = valu_group_template(g) != 0;
@@ -162,6 +168,8 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
 
   memset(out, 0, sizeof(*out));
   const int g = prob->num_q_heads / prob->num_kv_heads;
+  const int qn = prob->q_len > 1 ? prob->q_len : 1;     // query rows per sequence
+  const int R = g * qn;                                 // state rows per (sequence, KV head)
   const int elt = dtype_size(prob->kv_dtype);
   const int D = prob->head_dim;
   const int64_t max_len = prob->max_seq_len;
@@ -263,14 +271,14 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
         for (;;) {
           const int64_t s_try = cdiv64(max_len, chunk);
           if (s_try <= (max_splits > 0 ? max_splits : 1) &&
-              (s_try == 1 || ws_ratio((int)s_try, g, D, elt, max_len) <= budget))
+              (s_try == 1 || ws_ratio((int)s_try, R, D, elt, max_len) <= budget))
             break;
           chunk += align;
         }
       }
     } else {
       const int64_t n_blocks = max_len > 0 ? cdiv64(max_len, block) : 0;
-      S = split_rule(work, slots, n_blocks, max_splits, g, D, elt, max_len, budget, threshold);
+      S = split_rule(work, slots, n_blocks, max_splits, R, D, elt, max_len, budget, threshold);
       chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
     }
     S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
@@ -292,7 +300,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
   out->grid_y = nwg > 0 ? 1 : prob->num_kv_heads;
   out->grid_z = nwg > 0 ? 1 : prob->batch;
   out->scale = prob->scale != 0.0f ? prob->scale : (float)(1.0 / sqrt((double)D));
-  const int64_t heads = (int64_t)prob->batch * prob->num_q_heads;
+  const int64_t heads = (int64_t)prob->batch * qn * prob->num_q_heads;
   out->ws_o_bytes = heads * S * D * 4;
   out->ws_stats_bytes = heads * S * (o->ws_format == FD_WS_UML ? 2 : 1) * 4;
   out->ws_counter_bytes = (int64_t)prob->batch * prob->num_kv_heads * 4;

@@ -96,11 +96,13 @@ template <int D> struct Smem {
   float st_l[NW][16];
 };
 
-// Tokens [start, end) of segment (b, kvh), end > start, for the g query heads
-// of the group; the state goes to split slot `slot`.
+// Tokens [start, end) of segment (b, kvh), end > start, for the R = g * q_len
+// query rows of the group (MFMA column c: block row c / g, head c % g); the
+// state goes to split slot `slot`. Block row i sees tokens below vis0 + i
+// (vis0 = seq_len - (q_len - 1)).
 template <int D, typename T, bool PAGED>
 __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, int b, int kvh, int start, int end,
-                                            int slot) {
+                                            int slot, int vis0) {
   using G = Geo<D>;
   using V8 = typename Mma<T>::vec;
   using VR = typename VRead<G::VW>::type;
@@ -111,16 +113,21 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
+  const int R = p.R;             // query rows of the group (g heads x q_len block rows)
   const int col = lane & 15;     // MFMA column = query column
   const int grp = lane >> 4;     // 16-lane group
   const int ntiles = (end - start + TT - 1) / TT;
 
   // ---- Q^T as the B operand of S^T = K Q^T: column col holds head h(col).
-  const int hcol = col < g ? col : (col < 2 * g ? col - g : -1);
+  const int hcol = col < R ? col : (col < 2 * R ? col - R : -1);
+  const int qi = hcol < 0 ? p.q_len - 1 : hcol / g;          // block row of this column
+  const int col_end = min(end, vis0 + qi);                    // first token this column may not see
+  const int mask_from = min(end, vis0);                       // first token any column may not see
   V8 qb[G::NDC];
   {
-    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb +
-                    (int64_t)(kvh * g + (hcol < 0 ? 0 : hcol)) * p.q_sh;
+    const int hh = hcol < 0 ? 0 : hcol - qi * g;
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb + (int64_t)qi * p.q_sq +
+                    (int64_t)(kvh * g + hh) * p.q_sh;
 #pragma unroll
     for (int c = 0; c < G::NDC; ++c) {
       V8 v = *reinterpret_cast<const V8*>(qrow + 32 * c + 8 * grp);
@@ -219,39 +226,43 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[tb * 4 + i] = sacc[tb][i] * c2;
-    if (t0 + TT > end) {                      // tail tile: mask rows past the split
+    if (t0 + TT > mask_from) {                // tail tile: mask tokens a column may not see
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + tb * 16 + 4 * grp + i >= end) x[tb * 4 + i] = -INFINITY;
+          if (t0 + tb * 16 + 4 * grp + i >= col_end) x[tb * 4 + i] = -INFINITY;
     }
     float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);    // finite: row t0 is always valid
+    // A column of a query block can see no token of a tile (its max stays
+    // -inf): the rescale and the exponent then use safe references, so
+    // e^(-inf - (-inf)) is never formed.
+    const float m_new = fmaxf(m_run, mt);
     if (__any(m_new > m_run)) {
-      const float alpha = exp2_fast(m_run - m_new);
+      const float alpha = m_new > m_run ? exp2_fast(m_run - m_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < G::NDB; ++i) oacc[i] *= alpha;
       m_run = m_new;
     }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float pe[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pe[e] = exp2_fast(x[e] - m_run);
+      pe[e] = exp2_fast(x[e] - m_ref);
       psum += pe[e];
     }
     l_run += psum;
 
-    // ---- P^T as the B operand: high part in columns < g, remainder after.
+    // ---- P^T as the B operand: high part in columns < R, remainder after.
     V8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const T hi = (T)pe[e];
-      const float r = col < g ? pe[e] : pe[e] - (float)hi;
+      const float r = col < R ? pe[e] : pe[e] - (float)hi;
       pb[e] = (T)r;
     }
 
@@ -320,8 +331,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
 
   // ---- merge the four wave states (exact rescale to the common max) and
   // combine the high/low columns, then write the split's state.
-  const int Hq = p.Hq;
-  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < R * D; idx += NW * 64) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
@@ -334,11 +344,11 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
         const float mw = st_m[w2][h];
         const float a = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
         const float* o = reinterpret_cast<const float*>(lds[w2][0]);
-        U += a * (o[h * D + d] + o[(h + g) * D + d]);
+        U += a * (o[h * D + d] + o[(h + R) * D + d]);
         L += a * st_l[w2][h];
       }
     }
-    const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + slot;
+    const int64_t base = state_row(p, b, kvh, h) * p.S + slot;
     const bool co = p.fused != 0;
     if (p.ws_format == FD_WS_UML) {
       ws_store(p.ws_o + base * D + d, U, co);
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, seq_len);
   if (end > start)
-    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s);
+    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1));
   else
     write_neutral<D, NW * 64>(p, b, kvh, s, s + 1);
   if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
@@ -378,14 +388,14 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
   __shared__ Smem<D> sm;
   balanced_walk<NW * 64>(
       p,
-      [&](int b, int kvh, int start, int end, int slot, int count, bool last) {
+      [&](int b, int kvh, int start, int end, int slot, int count, bool last, int len) {
         b = __builtin_amdgcn_readfirstlane(b);
         kvh = __builtin_amdgcn_readfirstlane(kvh);
         start = __builtin_amdgcn_readfirstlane(start);
         end = __builtin_amdgcn_readfirstlane(end);
         slot = __builtin_amdgcn_readfirstlane(slot);
         if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
-        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot);
+        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1));
         if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
         if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
         __syncthreads();                         // LDS is reused by the next piece

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
+  const int R = p.R;             // query rows of the group: g heads x q_len block rows (<= G)
   const int rg = lane / LPR;     // row group
   const int li = lane % LPR;     // lane inside the row
 
@@ -136,14 +137,21 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int end = min(start + p.chunk, seq_len);
   const int ntiles = end > start ? (end - start + TT - 1) / TT : 0;
 
-  // q slices of the G heads of this group (heads >= g read as zero)
+  // q slices of the R query rows of this group (row r: block row r / g, head
+  // r % g; rows >= R read as zero). Block row i sees tokens below vis0 + i.
+  const int vis0 = seq_len - (p.q_len - 1);
+  const int mask_from = min(end, vis0);
   u32x4 q[G];
+  int row_end[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb +
-                    (int64_t)(kvh * g + (h < g ? h : 0)) * p.q_sh;
+    const int r = h < R ? h : 0;
+    const int i = r / g;
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb + (int64_t)i * p.q_sq +
+                    (int64_t)(kvh * g + r - i * g) * p.q_sh;
     u32x4 v = *reinterpret_cast<const u32x4*>(qrow + li * EPL);
-    q[h] = h < g ? v : u32x4{0u, 0u, 0u, 0u};
+    q[h] = h < R ? v : u32x4{0u, 0u, 0u, 0u};
+    row_end[h] = min(end, vis0 + i);
   }
 
   const char* kbase;
@@ -221,13 +229,13 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + offset(tn0, u, pid_next)));
     }
-    const bool tail = t0 + TT > end;
+    const bool tail = t0 + TT > mask_from;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float v = rowsum<LPR>(x[h][u]) * c2;
-        if (tail && t0 + u * RPI + rg >= end) v = -INFINITY;
+        if (tail && t0 + u * RPI + rg >= row_end[h]) v = -INFINITY;
         x[h][u] = v;
       }
 
@@ -290,8 +298,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   }
   __syncthreads();
 
-  const int Hq = p.Hq;
-  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < R * D; idx += NW * 64) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
           L += a * st_l[w][r][h];
         }
     }
-    const int64_t base = ((int64_t)b * Hq + kvh * g + h) * p.S + s;
+    const int64_t base = state_row(p, b, kvh, h) * p.S + s;
     const bool co = p.fused != 0;
     if (p.ws_format == FD_WS_UML) {
       ws_store(p.ws_o + base * D + d, Uv, co);

@@ -41,7 +41,7 @@ class Workload:
     """One decode step's inputs. Tensors live on ``device``."""
 
     name: str
-    q: torch.Tensor                 # [B, Hq, D]
+    q: torch.Tensor                 # [B, Hq, D], or [B, q_len, Hq, D] for a short query block
     k: torch.Tensor                 # contiguous [B, Hkv, T, D] or pool [P, page, Hkv, D]
     v: torch.Tensor
     seq_lens: torch.Tensor          # int32 [B]
@@ -60,11 +60,15 @@ class Workload:
 
     @property
     def num_q_heads(self) -> int:
-        return self.q.shape[1]
+        return self.q.shape[-2]
+
+    @property
+    def q_len(self) -> int:
+        return self.q.shape[1] if self.q.dim() == 4 else 1
 
     @property
     def head_dim(self) -> int:
-        return self.q.shape[2]
+        return self.q.shape[-1]
 
     @property
     def paged(self) -> bool:
@@ -105,12 +109,14 @@ def _randn(gen: torch.Generator, shape, dtype, device, gain: float = 1.0) -> tor
 def contiguous(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int,
                head_dim: int, capacity: int, seq_lens, dtype: str = "f16",
                q_gain: float = 1.0, k_gain: float = 1.0, device="cpu",
-               num_splits: int = 0, chunk_tokens: int = 0, ws_format: str = "uml") -> Workload:
-    """Contiguous-cache workload. ``seq_lens`` is a list or int32 tensor of length B."""
+               num_splits: int = 0, chunk_tokens: int = 0, ws_format: str = "uml", q_len: int = 1) -> Workload:
+    """Contiguous-cache workload. ``seq_lens`` is a list or int32 tensor of length B.
+    ``q_len`` > 1 draws a short query block q [B, q_len, Hq, D]."""
     dt = DTYPES[dtype]
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    q = _randn(gen, (batch, q_heads, head_dim), dt, device, q_gain)
+    qshape = (batch, q_len, q_heads, head_dim) if q_len > 1 else (batch, q_heads, head_dim)
+    q = _randn(gen, qshape, dt, device, q_gain)
     k = _randn(gen, (batch, kv_heads, capacity, head_dim), dt, device, k_gain)
     v = _randn(gen, (batch, kv_heads, capacity, head_dim), dt, device)
     sl = torch.as_tensor(seq_lens, dtype=torch.int32).to(device)
@@ -131,7 +137,7 @@ def _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, layout, gai
 def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head_dim: int,
           seq_lens, page_size: int = 16, dtype: str = "f16", device="cpu",
           num_splits: int = 0, chunk_tokens: int = 0, extra_pages: int = 0,
-          pool_layout: str = "hnd") -> Workload:
+          pool_layout: str = "hnd", q_len: int = 1) -> Workload:
     """Paged-pool workload: the pool holds exactly sum_b cdiv(len_b, page) pages
     (+ ``extra_pages`` unused ones); a seeded ``randperm`` of the pool is dealt
     out to the sequences in order, so each sequence's pages are scattered."""
@@ -150,7 +156,7 @@ def paged(name: str, *, seed: int, batch: int, q_heads: int, kv_heads: int, head
         cursor += n
     gen = torch.Generator(device=device)
     gen.manual_seed(seed + 1000)
-    q = _randn(gen, (batch, q_heads, head_dim), dt, device)
+    q = _randn(gen, (batch, q_len, q_heads, head_dim) if q_len > 1 else (batch, q_heads, head_dim), dt, device)
     k = _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, pool_layout)
     v = _pool(gen, num_pages, page_size, kv_heads, head_dim, dt, device, pool_layout)
     return Workload(name, q, k, v, sl.to(device), block_table=table.to(device),

@@ -147,7 +147,16 @@ typedef struct {
   int64_t pool_stride_t;
   int64_t pool_stride_h;
   float scale;            /* score scale; 0 selects 1/sqrt(D) */
-  int32_t reserved0;
+  /* Short query blocks (speculative decode; kanthi.in §7 "Short query blocks",
+   * §9 item 1: q is [B, q_len, Hq, D]). The block is the last q_len positions
+   * of each sequence, whose K/V are already in the cache: query row i sees
+   * tokens [0, seq_len - (q_len - 1 - i)) (each query keeps its own
+   * visibility, xuujii §06); a row that sees nothing gets O = 0, LSE = -inf.
+   * Needs g * q_len <= 8 (MFMA kernel, 16-bit caches) or <= 4 (VALU kernel).
+   * out and lse gain the same row axis: [B, q_len, Hq, D] and [B, q_len, Hq];
+   * the workspace holds B * q_len * Hq rows. */
+  int32_t q_len;          /* query rows per sequence; 0 or 1: a single query */
+  int64_t q_stride_q;     /* q[b, i, h, d] at q + b*q_stride_b + i*q_stride_q + h*q_stride_h + d */
 } fd_problem;
 
 /* Planner options. Zero-initialise for the defaults. */

@@ -52,8 +52,8 @@ def run(w, stream=None, **over):
     prob = fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale)
     plan = fd.fd_plan(prob, **opts)
     ws_o, ws_stats = fd.workspace(plan, dev)
-    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=dev)
-    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    out = torch.empty(*q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=dev)
     fd.fd_decode_split(plan, q, k, v, sl, ws_o, ws_stats, bt, stream)
     fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
     torch.cuda.synchronize()
@@ -72,8 +72,8 @@ def run_fused(w, ctr=None, **over):
     plan = fd.fd_plan(fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len, scale=w.scale), **opts)
     ws_o, ws_stats = fd.workspace(plan, dev)
     ctr = fd.counters(plan, dev) if ctr is None else ctr
-    out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=dev)
-    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    out = torch.empty(*q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=dev)
     fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse, bt)
     torch.cuda.synchronize()
     return plan, out.cpu(), lse.cpu(), ctr
@@ -112,6 +112,13 @@ def compare(out: torch.Tensor, lse: torch.Tensor, O: np.ndarray, LSE: np.ndarray
 
 
 def check_against_oracle(w, out, lse, pairs=None, **tol):
+    if w.q.dim() == 4:                       # short query block: rows (b, i) flattened
+        B, q_len, Hq, D = w.q.shape
+        rows = None if pairs is None else [(b, i, h) for b, h in pairs for i in range(q_len)]
+        O, LSE = A.decode_attention_block(w.q, w.k, w.v, w.seq_lens, w.block_table, w.scale or None, rows)
+        flat = None if pairs is None else [(b * q_len + i, h) for b, h in pairs for i in range(q_len)]
+        return compare(out.reshape(B * q_len, Hq, D), lse.reshape(B * q_len, Hq), O.reshape(B * q_len, Hq, D),
+                       LSE.reshape(B * q_len, Hq), flat, label=w.name, **tol)
     O, LSE = A.decode_attention(cache_of(w), pairs)
     return compare(out, lse, O, LSE, pairs, label=w.name, **tol)
 

@@ -330,6 +330,37 @@ def test_merge_states_validation_without_gpu():
         fd.fd_merge_states(torch.zeros(3, 4, 128), torch.zeros(3, 4), ws_format="uml")
 
 
+def test_query_block_problems():
+    """Short query blocks: validation, kernel choice by rows per KV head
+    (g * q_len), workspace rows and the q_len = 1 equivalence."""
+    def qb(q_len, Hq=8, Hkv=4, dtype=1, stride_q=None):
+        p = contiguous_problem(Hq=Hq, Hkv=Hkv, L=500, dtype=dtype)
+        p.q_len = q_len
+        p.q_stride_q = Hq * 128 if stride_q is None else stride_q
+        p.q_stride_b = q_len * Hq * 128
+        return p
+    assert fd.fd_plan(qb(4), num_cus=256).kernel == fd.KERNELS["mfma"]          # g=2, R=8
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(qb(5), num_cus=256)                                          # R=10 > 8
+    assert fd.fd_plan(qb(8, Hq=4, Hkv=4), num_cus=256, kernel="mfma").kernel == fd.KERNELS["mfma"]
+    assert fd.fd_plan(qb(2, Hq=4, Hkv=4, dtype=0), num_cus=256).kernel == fd.KERNELS["valu"]   # fp32: VALU
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(qb(8, Hq=4, Hkv=4, dtype=0), num_cus=256)                   # fp32, R=8 > 4
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(qb(9, Hq=4, Hkv=4), num_cus=256)                             # q_len > 8
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(qb(2, stride_q=1028), num_cus=256)                           # misaligned row stride
+    p = fd.fd_plan(qb(3), num_cus=256, force_splits=2)
+    assert p.ws_o_bytes == 3 * 8 * 2 * 128 * 4 and p.ws_stats_bytes == 3 * 8 * 2 * 2 * 4
+    a = fd.fd_plan(qb(1), num_cus=256)
+    b = fd.fd_plan(qb(0), num_cus=256)
+    assert (a.num_splits, a.chunk_tokens, a.ws_o_bytes) == (b.num_splits, b.chunk_tokens, b.ws_o_bytes)
+    q = torch.zeros(2, 3, 8, 128, dtype=torch.float16)
+    k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)
+    pr = fd.problem_for(q, k, k, torch.tensor([300, 2], dtype=torch.int32))
+    assert (pr.q_len, pr.q_stride_q, pr.q_stride_h, pr.q_stride_b) == (3, 8 * 128, 128, 3 * 8 * 128)
+
+
 def test_problem_for_tensors():
     q = torch.zeros(2, 16, 128, dtype=torch.float16)
     k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)
