@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "fd_internal.h"
 
 namespace fd {
@@ -57,6 +60,39 @@ int hip_fail(int err, const char* where) {
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Per-device cache of the CU count and of each split-kernel variant's
+// resident workgroups per CU: the occupancy query costs about a millisecond,
+// and a decode loop plans every step.
+struct DeviceInfo {
+  int num_cus = 0;
+  std::map<int, int> resident;       // variant key -> resident workgroups per CU
+};
+std::mutex g_dev_mutex;
+std::map<int, DeviceInfo> g_dev;
+
+int device_query(int dev, int kernel, int head_dim, int kv_dtype, int layout, int gtpl, int* num_cus,
+                 int* resident) {
+  const int key = (((kernel * 256 + head_dim) * 4 + kv_dtype) * 2 + layout) * 8 + gtpl;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& info = g_dev[dev];
+  if (info.num_cus == 0) {
+    int n = 0;
+    int err = (int)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err) return err;
+    info.num_cus = n;
+  }
+  auto it = info.resident.find(key);
+  if (it == info.resident.end()) {
+    int r = 0;
+    int err = occupancy_split(kernel, head_dim, kv_dtype, layout, gtpl, &r);
+    if (err) return err;
+    it = info.resident.emplace(key, r).first;
+  }
+  *num_cus = info.num_cus;
+  *resident = it->second;
+  return 0;
+}
 
 int check_plan(const fd_plan_t* plan) {
   if (!plan) return FD_ERR_INVALID_ARG;
@@ -124,23 +160,21 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   // else the table generated from the compiler's resource usage.
   int resident = 0;
   if (o.num_cus == 0) {
-    int dev = 0, n = 0;
+    int dev = 0;
     int err = (int)hipGetDevice(&dev);
     if (err) return hip_fail(err, "hipGetDevice");
-    err = (int)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err) return hip_fail(err, "hipDeviceGetAttribute");
-    o.num_cus = n;
-    err = occupancy_split(kernel, prob->head_dim, prob->kv_dtype, prob->layout, gtpl, &resident);
-    if (err) return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    err = device_query(dev, kernel, prob->head_dim, prob->kv_dtype, prob->layout, gtpl, &o.num_cus, &resident);
+    if (err) return hip_fail(err, "device query (CU count, occupancy)");
   }
   if (resident <= 0) resident = default_wgs_per_cu(kernel, prob->head_dim, prob->kv_dtype, gtpl, prob->layout);
   // Workgroups per CU in one wave of the MI355X split rule: 1 by default (one
   // streaming split workgroup per CU saturates its share of HBM; measured by
   // split-count sweeps), never more than can be resident.
+  const int balanced_wgs = o.wgs_per_cu > 0 ? (o.wgs_per_cu < resident ? o.wgs_per_cu : resident) : resident;
   if (o.wgs_per_cu == 0) o.wgs_per_cu = 1;
   if (o.wgs_per_cu > resident) o.wgs_per_cu = resident;
   o.kernel = kernel;
-  return plan_core(prob, &o, out);
+  return plan_core(prob, &o, balanced_wgs, out);
 }
 
 namespace {

@@ -63,8 +63,10 @@ int valu_group_template(int g);                 // 1, 2 or 4; 0 if unsupported
 int default_wgs_per_cu(int kernel, int head_dim, int kv_dtype, int group_tpl, int layout);
 
 // The pure host planner (no HIP calls). opts must be fully resolved:
-// num_cus > 0 and wgs_per_cu > 0.
-int plan_core(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* out);
+// num_cus > 0 and wgs_per_cu > 0. balanced_wgs_per_cu: workgroups per CU of
+// the balanced grid (the caller's wgs_per_cu if it set one, else every
+// workgroup the kernel can keep resident).
+int plan_core(const fd_problem* prob, const fd_plan_opts* opts, int balanced_wgs_per_cu, fd_plan_t* out);
 int validate_problem(const fd_problem* prob);
 int choose_kernel(const fd_problem* prob, int requested);
 uint64_t plan_checksum(const fd_plan_t* plan);

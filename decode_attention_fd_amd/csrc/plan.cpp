@@ -145,7 +145,7 @@ uint64_t plan_checksum(const fd_plan_t* plan) {
   return h;
 }
 
-int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
+int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_per_cu, fd_plan_t* out) {
   if (!prob || !o || !out) return FD_ERR_INVALID_ARG;
   int st = validate_problem(prob);
   if (st != FD_OK) return st;
@@ -202,7 +202,9 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, fd_plan_t* out) {
       // The line of granules (see fd_schedule): N workgroups, range w =
       // [floor(w T / N), floor((w + 1) T / N)); S = the most ranges that any
       // one segment meets.
-      slots = (int64_t)o->num_cus * o->wgs_per_cu;
+      // Two resident ranges per CU overlap one range's start-up and drain with
+      // the other's streaming (measured: 219 vs 229-241 us on the paged batch).
+      slots = (int64_t)o->num_cus * (balanced_wgs_per_cu > 0 ? balanced_wgs_per_cu : o->wgs_per_cu);
       const int64_t G = tile > paged_align ? tile : paged_align;
       const int64_t H = prob->num_kv_heads;
       int64_t T = 0;

@@ -114,7 +114,8 @@ typedef enum {
   /* Needs host_seq_lens. The batch's (sequence, KV head) segments, each cut
    * into granules of G tokens (G = the wave tile, or the page if larger), are
    * laid end to end and cut into N near-equal ranges, one per workgroup
-   * (N = min(slots, cdiv(total granules, 4))). A segment crossing a range
+   * (N = min(CUs x resident workgroups per CU, or CUs x wgs_per_cu when the
+   * caller sets it, and cdiv(total granules, 4))). A segment crossing a range
    * boundary yields one state per range; kanthi.in §6 asks for per-sequence
    * split counts on ragged batches, and this is such a count, chosen so that
    * every workgroup streams the same number of bytes. */

@@ -179,7 +179,8 @@ def test_balanced_schedule_matches_oracle(paged):
         plan = fd.fd_plan(prob, num_cus=cus, host_seq_lens=lens, schedule="balanced")
         assert plan.schedule == fd.SCHEDULES["balanced"]
         G = max(32, page)
-        N, S, _ = OP.balanced_schedule(lens, Hkv, G, cus)
+        assert plan.slots == cus * 2                   # two resident D=128 16-bit workgroups per CU
+        N, S, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots)
         assert (plan.grid_x, plan.grid_y, plan.grid_z) == (N, 1, 1), (lens, cus)
         assert plan.num_splits == S and plan.chunk_tokens == G
         assert plan.ws_o_bytes == B * Hkv * g * S * 128 * 4
