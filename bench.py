@@ -157,8 +157,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = planner)")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate (0 = enough for 2x the MALL)")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
-    ap.add_argument("--path", choices=["fused", "split"], default="split",
-                    help="fused: one launch (last workgroup per group merges); split: split + merge kernels")
+    ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
+                    help="fused: one launch (last workgroup per group merges); split: split + merge kernels; "
+                         "auto: fused when the plan has one split (the rows are written directly), else split")
     ap.add_argument("--schedule", choices=["auto", "uniform", "balanced"], default="auto",
                     help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner slots per CU (0 = library default)")
@@ -216,12 +217,13 @@ def main():
     out = torch.empty(w0.batch, w0.num_q_heads, w0.head_dim, dtype=torch.float32, device=dev)
     lse = torch.empty(w0.batch, w0.num_q_heads, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    path = args.path if args.path != "auto" else ("fused" if plan.num_splits == 1 else "split")
 
     def step(i, evs=None):
         w = ws[i % copies]
         if evs is not None:
             evs[0].record(stream)
-        if args.path == "fused":
+        if path == "fused":
             fd.fd_decode_fused(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, ctr, out, lse, w.block_table, stream)
             if evs is not None:
                 evs[1].record(stream)
@@ -287,7 +289,7 @@ def main():
             "kv_bytes_allocated": alloc, "kv_copies": copies, "layout": "paged" if w0.paged else "contiguous",
             "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
             "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
-            "slots": plan.slots, "plan_us": round(plan_us, 1), "path": args.path,
+            "slots": plan.slots, "plan_us": round(plan_us, 1), "path": path,
             "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "grid": plan.grid_x * plan.grid_y * plan.grid_z,
         },
         "split_kernel_us": round(split_us, 2),

@@ -301,13 +301,16 @@ def fd_merge_states(states, stats, out=None, lse_out=None, *, ws_format: str = "
 
 
 def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,
-                 return_lse: bool = True, fused: bool = False, stream=None, **plan_options):
-    """Plan, split and merge (two launches, or one with ``fused=True``); returns
-    (out, lse) fp32 (lse None if not asked)."""
+                 return_lse: bool = True, fused: Optional[bool] = None, stream=None, **plan_options):
+    """Plan, split and merge (two launches, or one with ``fused=True``; by
+    default one when the plan has a single split, whose rows the split kernel
+    then writes directly); returns (out, lse) fp32 (lse None if not asked)."""
     plan = fd_plan(problem_for(q, k, v, seq_lens, block_table, max_seq_len, scale), **plan_options)
     ws_o, ws_stats = workspace(plan, q.device)
     out = torch.empty(*q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=q.device) if return_lse else None
+    if fused is None:
+        fused = plan.num_splits == 1
     if fused:
         fd_decode_fused(plan, q, k, v, seq_lens, ws_o, ws_stats, counters(plan, q.device), out, lse, block_table,
                         stream)

@@ -2,11 +2,11 @@
 //
 // The uniform schedule cuts every (sequence, KV head) segment into splits of
 // one fixed chunk; with ragged lengths the launch then holds many workgroups
-// of very different sizes and the longest sequences decide the time ("Flash-
-// Decoding: Split-KV Attention for Long-Context Decode", kanthi.in, §6 notes
-// that variable-length batches want per-sequence split counts; FlashInfer's
-// planner, as described on "FlashInfer Attention States" and the xuujii KB
-// "Decode 专项 Attention" §07, balances work across CTAs instead).
+// of very different sizes and the longest sequences decide the time. The
+// pages point at two remedies: a split plan made for the current batch,
+// heads and lengths (xuujii KB "Decode 专项 Attention" §07) and Stream-K-style
+// work partitioning against wave quantization (LeanAttention, listed in
+// "Flash-Decoding: Split-KV Attention for Long-Context Decode", kanthi.in, §7).
 //
 // Here the whole batch is one line of granules: segment (b, h) is
 // cdiv(len_b, G) granules of G tokens, segments in (b, h) order. A grid of N
@@ -54,6 +54,16 @@ __device__ __forceinline__ void write_neutral(const SplitParams& p, int b, int k
         ws_store(p.ws_stats + base, -INFINITY, co);
       }
     }
+  }
+}
+
+// The finished rows of an empty group (b, kvh) in a fused call: O = 0, LSE = -inf.
+template <int D, int NTHREADS>
+__device__ __forceinline__ void empty_group(const SplitParams& p, int b, int kvh) {
+  for (int i = threadIdx.x; i < p.R * D; i += NTHREADS) {
+    const int64_t row = state_row(p, b, kvh, i / D);
+    p.out[row * D + i % D] = 0.f;
+    if (p.lse && i % D == 0) p.lse[row] = -INFINITY;
   }
 }
 

@@ -98,11 +98,12 @@ template <int D> struct Smem {
 
 // Tokens [start, end) of segment (b, kvh), end > start, for the R = g * q_len
 // query rows of the group (MFMA column c: block row c / g, head c % g); the
-// state goes to split slot `slot`. Block row i sees tokens below vis0 + i
-// (vis0 = seq_len - (q_len - 1)).
+// state goes to split slot `slot`, or, with `direct` (the segment's only
+// piece, fused call), straight to out/lse as the finished rows. Block row i
+// sees tokens below vis0 + i (vis0 = seq_len - (q_len - 1)).
 template <int D, typename T, bool PAGED>
 __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, int b, int kvh, int start, int end,
-                                            int slot, int vis0) {
+                                            int slot, int vis0, bool direct) {
   using G = Geo<D>;
   using V8 = typename Mma<T>::vec;
   using VR = typename VRead<G::VW>::type;
@@ -348,9 +349,14 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
         L += a * st_l[w2][h];
       }
     }
-    const int64_t base = state_row(p, b, kvh, h) * p.S + slot;
+    const int64_t row = state_row(p, b, kvh, h);
+    const int64_t base = row * p.S + slot;
     const bool co = p.fused != 0;
-    if (p.ws_format == FD_WS_UML) {
+    if (direct) {                              // one piece: the state is the row's result
+      const bool empty = !(L > 0.f);
+      p.out[row * D + d] = empty ? 0.f : U / L;
+      if (d == 0 && p.lse) p.lse[row] = empty ? -INFINITY : (M + log2f(L)) * LN2;
+    } else if (p.ws_format == FD_WS_UML) {
       ws_store(p.ws_o + base * D + d, U, co);
       if (d == 0) {
         ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
@@ -375,11 +381,14 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, seq_len);
+  const bool direct = p.fused && p.S == 1;
   if (end > start)
-    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1));
+    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
+  else if (direct)
+    empty_group<D, NW * 64>(p, b, kvh);
   else
     write_neutral<D, NW * 64>(p, b, kvh, s, s + 1);
-  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+  if (p.fused && !direct) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
 }
 
 // Balanced schedule: workgroup w owns an equal share of the batch's granules.
@@ -395,9 +404,12 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
         end = __builtin_amdgcn_readfirstlane(end);
         slot = __builtin_amdgcn_readfirstlane(slot);
         if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
-        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1));
-        if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
-        if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+        const bool direct = p.fused && count == 1;
+        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
+        if (!direct) {
+          if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
+          if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+        }
         __syncthreads();                         // LDS is reused by the next piece
       },
       [&](int b) { empty_row<D, NW * 64>(p, b); });

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, seq_len);
   const int ntiles = end > start ? (end - start + TT - 1) / TT : 0;
+  const bool direct = p.fused && p.S == 1;    // fused call with one split: write out/lse directly
 
   // q slices of the R query rows of this group (row r: block row r / g, head
   // r % g; rows >= R read as zero). Block row i sees tokens below vis0 + i.
@@ -318,9 +319,14 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
           L += a * st_l[w][r][h];
         }
     }
-    const int64_t base = state_row(p, b, kvh, h) * p.S + s;
+    const int64_t row = state_row(p, b, kvh, h);
+    const int64_t base = row * p.S + s;
     const bool co = p.fused != 0;
-    if (p.ws_format == FD_WS_UML) {
+    if (direct) {                              // one split: the state is the row's result
+      const bool empty = !(L > 0.f);
+      p.out[row * D + d] = empty ? 0.f : Uv / L;
+      if (d == 0 && p.lse) p.lse[row] = empty ? -INFINITY : (M + log2f(L)) * LN2;
+    } else if (p.ws_format == FD_WS_UML) {
       ws_store(p.ws_o + base * D + d, Uv, co);
       if (d == 0) {
         ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
       if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
-  if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+  if (p.fused && !direct) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
 }
 
 template <int D, typename T, int G>

@@ -116,9 +116,9 @@ typedef enum {
    * laid end to end and cut into N near-equal ranges, one per workgroup
    * (N = min(CUs x resident workgroups per CU, or CUs x wgs_per_cu when the
    * caller sets it, and cdiv(total granules, 4))). A segment crossing a range
-   * boundary yields one state per range; kanthi.in §6 asks for per-sequence
-   * split counts on ragged batches, and this is such a count, chosen so that
-   * every workgroup streams the same number of bytes. */
+   * boundary yields one state per range: a Stream-K-style partition of the
+   * kind kanthi.in §7 lists (LeanAttention) against wave quantization, here
+   * so that every workgroup streams the same number of bytes. */
   FD_SCHEDULE_BALANCED = 2
 } fd_schedule;
 
@@ -242,10 +242,12 @@ FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_st
 
 /* Split kernel with the merge fused in: as fd_decode_split, and in addition the
  * workgroup that finishes last for each (sequence, KV head) merges that
- * group's split states and writes out/lse as fd_merge would (kanthi.in §9
- * decode contract names this "documented fused alternative"; its "Try this"
- * list describes the last-CTA merge with an atomic counter). One launch
- * instead of two. counters: uint32 [B * Hkv] (plan->ws_counter_bytes), all
+ * group's split states and writes out/lse as fd_merge would. A group that is
+ * one split only (S = 1, or one piece under the balanced schedule) writes its
+ * rows straight to out/lse and touches neither workspace nor counter. (kanthi.in
+ * §9 allows a fused combine in place of the separate one as long as it is
+ * documented; the chapter's exercises describe the last-CTA merge with an
+ * atomic counter.) One launch instead of two. counters: uint32 [B * Hkv] (plan->ws_counter_bytes), all
  * zero before the first call (allocate it zeroed); every call leaves them
  * zero again. Calls that share counters or workspace must not overlap in
  * time (issue them on one stream). out: float [B, Hq, D]; lse: float [B, Hq]
@@ -257,8 +259,8 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
 /* Merge externally produced attention states, one output per row: the ⊕
  * operator of kanthi.in §2 (stable form) exposed on its own, for cascade
  * attention over shared prefixes and for states gathered from other devices
- * (§7 "across GPUs"); FlashInfer's merge_state does the same on its page
- * "FlashInfer Attention States".
+ * (kanthi.in §2 and §7 apply the same merge across devices, and name
+ * FlashInfer's merge_state / merge_states as this operation).
  *   ws_format FD_WS_OLSE: states[r, s, :] is a normalised output o_s and
  *     stats[r, s] its natural-log LSE; O = sum_s w_s o_s / sum_s w_s with
  *     w_s = e^{lse_s - max lse}, LSE = max + ln(sum_s w_s).

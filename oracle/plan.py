@@ -120,8 +120,8 @@ def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_gran
     intersection of a range with a segment is one piece. Returns
     (N, S, pieces) with pieces[(b, h)] = [(w, token_lo, token_hi), ...] in
     workgroup order and S = the largest number of pieces of one segment (at
-    least 1). Variable-length batches want per-sequence split counts (kanthi.in
-    §6); this is one such count that gives every workgroup the same bytes.
+    least 1). It is a Stream-K-style partition of the kind kanthi.in §7 lists
+    (LeanAttention), one that gives every workgroup the same bytes.
     Parity unpinned as a performance choice; its partition is checked
     exhaustively in tests."""
     lens = [max(0, int(n)) for n in lengths]

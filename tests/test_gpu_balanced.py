@@ -104,3 +104,15 @@ def test_balanced_equals_uniform_bitwise_when_pieces_coincide():
     p2, o2, l2, _, _ = H.run(w, num_cus=64, schedule="uniform", host_seq_lens=None, force_chunk_tokens=4000)
     assert (p1.grid_x, p1.num_splits) == (64, 8) and p2.num_splits == 8
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_balanced_fused_mixes_direct_and_merged_groups():
+    """Three ranges over [2, 0, 1, 3]-granule rows (two KV heads): most groups
+    are one piece and are written directly, one crosses a range boundary and
+    goes through the counter and the merge."""
+    w = W.contiguous("mixed_direct", seed=98, batch=4, q_heads=8, kv_heads=2, head_dim=128, capacity=96,
+                     seq_lens=[64, 0, 32, 96], dtype="f16")
+    plan, out, lse, ctr = H.run_fused(w, num_cus=3, wgs_per_cu=1, schedule="balanced")
+    assert plan.schedule == BAL and plan.grid_x == 3 and plan.num_splits == 2
+    assert torch.all(ctr == 0).item()
+    H.check_against_oracle(w, out, lse)

@@ -322,3 +322,37 @@ def test_fused_agrees_with_two_launch_path():
     _, out_s, lse_s, _, _ = H.run(w)
     assert (out_f - out_s).abs().max().item() < 1e-5
     assert (lse_f - lse_s).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("case", ["mfma", "valu", "qblock", "zero_rows"])
+def test_fused_single_split_writes_rows_directly(case):
+    """A fused call whose plan has one split writes out/lse from the split
+    kernel's epilogue: the workspace is never touched (it stays NaN) and the
+    counters stay zero."""
+    if case == "mfma":
+        w = W.contiguous("direct_mfma", seed=85, batch=3, q_heads=32, kv_heads=4, head_dim=128, capacity=900,
+                         seq_lens=[900, 31, 400], dtype="bf16")
+    elif case == "valu":
+        w = W.contiguous("direct_valu", seed=86, batch=3, q_heads=4, kv_heads=4, head_dim=64, capacity=700,
+                         seq_lens=[700, 1, 65], dtype="f32")
+    elif case == "qblock":
+        w = W.contiguous("direct_qblock", seed=87, batch=3, q_heads=8, kv_heads=4, head_dim=128, capacity=500,
+                         seq_lens=[500, 2, 1], dtype="f16", q_len=3)
+    else:
+        w = W.contiguous("direct_zero", seed=88, batch=3, q_heads=16, kv_heads=2, head_dim=128, capacity=300,
+                         seq_lens=[0, 300, 0], dtype="f16")
+    dev = torch.device("cuda", 0)
+    q, k, v, sl = w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev)
+    plan = fd.fd_plan(fd.problem_for(q, k, v, sl), force_splits=1)
+    assert plan.num_splits == 1
+    ws_o, ws_stats = fd.workspace(plan, dev)
+    ws_o.fill_(float("nan"))
+    ws_stats.fill_(float("nan"))
+    ctr = fd.counters(plan, dev)
+    out = torch.empty(*q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=dev)
+    fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(ws_o)).item() and torch.all(torch.isnan(ws_stats)).item()
+    assert torch.all(ctr == 0).item()
+    H.check_against_oracle(w, out.cpu(), lse.cpu())
