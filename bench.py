@@ -56,11 +56,14 @@ def make_workload(name: str, device):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the MFMA split kernel is compiled from (the kernel
+    the roofline and the traffic record describe)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_attention_fd_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for rel in ("decode_attention_fd_amd/csrc/split_mfma.hip", "decode_attention_fd_amd/csrc/balance.h",
+                "decode_attention_fd_amd/csrc/merge_rows.h", "decode_attention_fd_amd/csrc/fd_internal.h",
+                "include/fd.h"):
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(rel.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -256,6 +259,27 @@ def main():
     merge_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     split_us = sum(split_ms) / len(split_ms) * 1e3
     merge_us = sum(merge_ms) / len(merge_ms) * 1e3
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+
+    def pct(xs, q):
+        return round(xs[min(len(xs) - 1, int(q * (len(xs) - 1) + 0.5))] * 1e3, 2)
+
+    # same-run streaming-read probe: two 512 MiB buffers in turn (each twice the MALL)
+    probe_bytes = 512 << 20
+    pbufs = [torch.empty(probe_bytes, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(2)]
+    sink = torch.empty(fd.READ_PROBE_SINK_BYTES // 4, dtype=torch.int32, device=dev)
+    for i in range(4):
+        fd.fd_read_probe(pbufs[i % 2], sink, stream)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    probe_iters = 20
+    pe[0].record(stream)
+    for i in range(probe_iters):
+        fd.fd_read_probe(pbufs[i % 2], sink, stream)
+    pe[1].record(stream)
+    torch.cuda.synchronize()
+    probe_us = pe[0].elapsed_time(pe[1]) * 1e3 / probe_iters
+    probe_gbps = probe_bytes / (probe_us * 1e-6) / 1e9
+    del pbufs
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -292,6 +316,7 @@ def main():
             "slots": plan.slots, "plan_us": round(plan_us, 1), "path": path,
             "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "grid": plan.grid_x * plan.grid_y * plan.grid_z,
         },
+        "step_event_us": {"p10": pct(step_ms, 0.1), "p50": pct(step_ms, 0.5), "p90": pct(step_ms, 0.9)},
         "split_kernel_us": round(split_us, 2),
         "merge_kernel_us": round(merge_us, 2),
         "merge_share": round(merge_us / max(split_us + merge_us, 1e-9), 4),
@@ -300,6 +325,8 @@ def main():
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
             "kernel": "split", "bytes_per_launch": step_kv, "kernel_source_hash": khash,
         },
+        "read_probe": {"value": round(probe_gbps, 1), "unit": "GB/s", "bytes": probe_bytes,
+                       "us": round(probe_us, 2), "split_kernel_frac_of_probe": round(achieved / probe_gbps, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -109,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge_states.restype = ctypes.c_int
+        L.fd_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]
+        L.fd_read_probe.restype = ctypes.c_int
         L.fd_status_str.argtypes = [ctypes.c_int]
         L.fd_status_str.restype = ctypes.c_char_p
         L.fd_last_hip_error.argtypes = []
@@ -298,6 +301,17 @@ def fd_merge_states(states, stats, out=None, lse_out=None, *, ws_format: str = "
                                _stream_handle(stream))
     _check(st, "fd_merge_states")
     return out, lse_out
+
+
+READ_PROBE_SINK_BYTES = 512 * 256 * 4
+
+
+def fd_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Launch the streaming-read probe over ``buf`` (device, bytes a multiple of
+    16); ``sink`` is an int32/uint32 device tensor of READ_PROBE_SINK_BYTES."""
+    st = lib().fd_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                             sink.numel() * sink.element_size(), _stream_handle(stream))
+    _check(st, "fd_read_probe")
 
 
 def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,

@@ -322,4 +322,13 @@ FD_API int fd_merge_states(int ws_format, const float* states, const float* stat
   return FD_OK;
 }
 
+FD_API int fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return FD_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return FD_ERR_ALIGNMENT;
+  if (sink_bytes < (size_t)FD_READ_PROBE_SINK_BYTES) return FD_ERR_WORKSPACE;
+  int err = launch_read_probe(buf, (int64_t)bytes, sink, FD_READ_PROBE_SINK_BYTES / (256 * 4), stream);
+  if (err) return hip_fail(err, "read probe launch");
+  return FD_OK;
+}
+
 }  // extern "C"

@@ -54,6 +54,7 @@ int launch_split_mfma(const SplitParams& p, int head_dim, int kv_dtype, int layo
 int launch_split_valu(const SplitParams& p, int head_dim, int kv_dtype, int layout, int group_tpl,
                       void* stream);
 int launch_merge(const MergeParams& p, int head_dim, void* stream);
+int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, void* stream);
 
 // Per-kernel geometry the planner needs (tokens per wave tile, waves per
 // workgroup) and the compiled resident-workgroups-per-CU of each variant.

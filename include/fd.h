@@ -277,6 +277,17 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
 FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,
                            int32_t num_states, int32_t head_dim, float* out, float* lse_out, void* stream);
 
+/* Measurement aid, not part of the attention path: a streaming-read kernel
+ * that reads `bytes` (a multiple of 16) of device memory at `buf` with the
+ * split kernels' load form (16-byte nontemporal loads, 512 workgroups each on
+ * a contiguous share), so a benchmark can report the read rate this device
+ * reaches next to its nominal peak (the chapter's benchmark plan, kanthi.in
+ * §8, judges kernels by achieved bandwidth against HBM peak). `sink` (device,
+ * at least FD_READ_PROBE_SINK_BYTES) receives one digest word per thread and
+ * nothing else. Time it with events on `stream`. */
+#define FD_READ_PROBE_SINK_BYTES (512 * 256 * 4)
+FD_API int fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream);
+
 /* Human-readable text for an fd_status. Never NULL. */
 FD_API const char* fd_status_str(int status);
 

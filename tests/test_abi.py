@@ -362,6 +362,17 @@ def test_query_block_problems():
     assert (pr.q_len, pr.q_stride_q, pr.q_stride_h, pr.q_stride_b) == (3, 8 * 128, 128, 3 * 8 * 128)
 
 
+def test_read_probe_validation_without_gpu():
+    L = fd.lib()
+    n = fd.READ_PROBE_SINK_BYTES
+    assert L.fd_read_probe(None, 1 << 20, 0x20000, n, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_read_probe(0x10000, 1 << 20, None, n, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_read_probe(0x10000, 8, 0x20000, n, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_read_probe(0x10000, (1 << 20) + 4, 0x20000, n, None) == fd.FD_ERR_INVALID_ARG
+    assert L.fd_read_probe(0x10008, 1 << 20, 0x20000, n, None) == fd.FD_ERR_ALIGNMENT
+    assert L.fd_read_probe(0x10000, 1 << 20, 0x20000, n - 4, None) == fd.FD_ERR_WORKSPACE
+
+
 def test_problem_for_tensors():
     q = torch.zeros(2, 16, 128, dtype=torch.float16)
     k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)

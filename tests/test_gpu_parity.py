@@ -356,3 +356,27 @@ def test_fused_single_split_writes_rows_directly(case):
     assert torch.all(torch.isnan(ws_o)).item() and torch.all(torch.isnan(ws_stats)).item()
     assert torch.all(ctr == 0).item()
     H.check_against_oracle(w, out.cpu(), lse.cpu())
+
+
+def test_read_probe_reads_every_byte():
+    """The streaming-read probe's per-thread digests equal the XOR of the
+    16-byte words each thread is assigned (so every byte was read)."""
+    n16 = 70001                                   # not a multiple of the grid
+    g = torch.Generator().manual_seed(99)
+    host = torch.randint(0, 2**31 - 1, (n16, 4), generator=g, dtype=torch.int64).to(torch.int32)
+    buf = host.to("cuda")
+    sink = torch.zeros(fd.READ_PROBE_SINK_BYTES // 4, dtype=torch.int32, device="cuda")
+    fd.fd_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    words = host.numpy().view(np.uint32)
+    grid, pt = fd.READ_PROBE_SINK_BYTES // (256 * 4), 256
+    per = -(-n16 // grid)
+    want = np.zeros(grid * pt, dtype=np.uint32)
+    for w in range(grid):
+        lo, hi = w * per, min(n16, w * per + per)
+        for t in range(pt):
+            idx = np.arange(lo + t, hi, pt)
+            if idx.size:
+                x = np.bitwise_xor.reduce(words[idx], axis=0)
+                want[w * pt + t] = x[0] ^ x[1] ^ x[2] ^ x[3]
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
