@@ -100,8 +100,7 @@ int check_plan(const fd_plan_t* plan) {
   if (validate_problem(&plan->prob) != FD_OK) return FD_ERR_BAD_PLAN;
   if (plan->num_splits < 1 || plan->chunk_tokens < 1) return FD_ERR_BAD_PLAN;
   if (plan->schedule != FD_SCHEDULE_UNIFORM && plan->schedule != FD_SCHEDULE_BALANCED) return FD_ERR_BAD_PLAN;
-  if (plan->schedule == FD_SCHEDULE_BALANCED && (plan->kernel != FD_KERNEL_MFMA || plan->grid_x < 1))
-    return FD_ERR_BAD_PLAN;
+  if (plan->schedule == FD_SCHEDULE_BALANCED && plan->grid_x < 1) return FD_ERR_BAD_PLAN;
   return FD_OK;
 }
 
@@ -170,7 +169,11 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   // Workgroups per CU in one wave of the MI355X split rule: 1 by default (one
   // streaming split workgroup per CU saturates its share of HBM; measured by
   // split-count sweeps), never more than can be resident.
-  const int balanced_wgs = o.wgs_per_cu > 0 ? (o.wgs_per_cu < resident ? o.wgs_per_cu : resident) : resident;
+  // The balanced kernels carry the walk's state on top of the split loop's and
+  // keep two workgroups per CU resident at most.
+  const int balanced_resident = resident < 2 ? resident : 2;
+  const int balanced_wgs =
+      o.wgs_per_cu > 0 ? (o.wgs_per_cu < balanced_resident ? o.wgs_per_cu : balanced_resident) : balanced_resident;
   if (o.wgs_per_cu == 0) o.wgs_per_cu = 1;
   if (o.wgs_per_cu > resident) o.wgs_per_cu = resident;
   o.kernel = kernel;

@@ -196,9 +196,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
        o->force_chunk_tokens <= 0 && o->heuristic == FD_HEURISTIC_MI355X && ragged &&
        (int64_t)prob->batch * prob->num_kv_heads <= (int64_t)o->num_cus * o->wgs_per_cu);
   if (balanced) {
-    if (kernel != FD_KERNEL_MFMA) {
-      if (o->schedule == FD_SCHEDULE_BALANCED) return FD_ERR_UNSUPPORTED;
-    } else {
+    {
       // The line of granules (see fd_schedule): N workgroups, range w =
       // [floor(w T / N), floor((w + 1) T / N)); S = the most ranges that any
       // one segment meets.

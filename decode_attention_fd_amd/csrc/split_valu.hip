@@ -19,6 +19,7 @@
 
 #include "fd_internal.h"
 #include "merge_rows.h"
+#include "balance.h"
 
 namespace fd {
 namespace {
@@ -113,34 +114,36 @@ template <int D, typename T> struct VGeo {
   static constexpr int ELT = sizeof(T);
 };
 
+template <int D, typename T, int G> struct VSmem {
+  float st_o[NW][VGeo<D, T>::RPI][G][D];
+  float st_m[NW][VGeo<D, T>::RPI][G];
+  float st_l[NW][VGeo<D, T>::RPI][G];
+};
+
+// Tokens [start, end) of segment (b, kvh) (possibly empty) for the R query
+// rows of the group; the state goes to split slot `slot`, or, with `direct`
+// (the segment's only piece, fused call), straight to out/lse. Block row i
+// sees tokens below vis0 + i.
 template <int D, typename T, int G, bool PAGED>
-__global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
+__device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>& sm, int b, int kvh, int start,
+                                           int end, int slot, int vis0, bool direct) {
   using VG = VGeo<D, T>;
   constexpr int EPL = VG::EPL, LPR = VG::LPR, RPI = VG::RPI, TT = VG::TT;
-  __shared__ float st_o[NW][RPI][G][D];
-  __shared__ float st_m[NW][RPI][G];
-  __shared__ float st_l[NW][RPI][G];
+  auto& st_o = sm.st_o;
+  auto& st_m = sm.st_m;
+  auto& st_l = sm.st_l;
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const int s = slot;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int g = p.g;
   const int R = p.R;             // query rows of the group: g heads x q_len block rows (<= G)
   const int rg = lane / LPR;     // row group
   const int li = lane % LPR;     // lane inside the row
-
-  int seq_len = p.seq_lens[b];
-  seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
-  const int start = s * p.chunk;
-  const int end = min(start + p.chunk, seq_len);
   const int ntiles = end > start ? (end - start + TT - 1) / TT : 0;
-  const bool direct = p.fused && p.S == 1;    // fused call with one split: write out/lse directly
 
   // q slices of the R query rows of this group (row r: block row r / g, head
   // r % g; rows >= R read as zero). Block row i sees tokens below vis0 + i.
-  const int vis0 = seq_len - (p.q_len - 1);
   const int mask_from = min(end, vis0);
   u32x4 q[G];
   int row_end[G];
@@ -338,17 +341,63 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
       if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
+}
+
+// Uniform schedule: workgroup (s, kvh, b) owns split s of segment (b, kvh).
+template <int D, typename T, int G, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
+  __shared__ VSmem<D, T, G> sm;
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  int seq_len = p.seq_lens[b];
+  seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
+  const int start = s * p.chunk;
+  const int end = min(start + p.chunk, seq_len);
+  const bool direct = p.fused && p.S == 1;    // fused call with one split: write out/lse directly
+  valu_piece<D, T, G, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
   if (p.fused && !direct) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+}
+
+// Balanced schedule: workgroup w owns an equal share of the batch's granules.
+template <int D, typename T, int G, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void split_valu_balanced_kernel(SplitParams p) {
+  __shared__ VSmem<D, T, G> sm;
+  balanced_walk<NW * 64>(
+      p,
+      [&](int b, int kvh, int start, int end, int slot, int count, bool last, int len) {
+        b = __builtin_amdgcn_readfirstlane(b);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        start = __builtin_amdgcn_readfirstlane(start);
+        end = __builtin_amdgcn_readfirstlane(end);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+        if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
+        const bool direct = p.fused && count == 1;
+        valu_piece<D, T, G, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
+        if (!direct) {
+          if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
+          if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+        }
+        __syncthreads();                         // LDS is reused by the next piece
+      },
+      [&](int b) { empty_row<D, NW * 64>(p, b); });
 }
 
 template <int D, typename T, int G>
 int launch_g(const SplitParams& p, bool paged, void* stream) {
-  dim3 grid(p.S, p.Hkv, p.B);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (paged)
-    hipLaunchKernelGGL((split_valu_kernel<D, T, G, true>), grid, dim3(NW * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((split_valu_kernel<D, T, G, false>), grid, dim3(NW * 64), 0, st, p);
+  if (p.nwg > 0) {
+    if (paged)
+      hipLaunchKernelGGL((split_valu_balanced_kernel<D, T, G, true>), dim3(p.nwg), dim3(NW * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((split_valu_balanced_kernel<D, T, G, false>), dim3(p.nwg), dim3(NW * 64), 0, st, p);
+  } else {
+    dim3 grid(p.S, p.Hkv, p.B);
+    if (paged)
+      hipLaunchKernelGGL((split_valu_kernel<D, T, G, true>), grid, dim3(NW * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((split_valu_kernel<D, T, G, false>), grid, dim3(NW * 64), 0, st, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -105,8 +105,7 @@ typedef enum {
 typedef enum {
   /* BALANCED when the planner has host_seq_lens, the lengths differ, there
    * are no more (sequence, KV head) segments than workgroup slots, no split
-   * count or chunk is forced, the MI355X rule is in use and the kernel
-   * supports it; else UNIFORM. */
+   * count or chunk is forced and the MI355X rule is in use; else UNIFORM. */
   FD_SCHEDULE_AUTO = 0,
   /* One workgroup per (split, KV head, sequence); split s of every segment is
    * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1). */
@@ -114,8 +113,8 @@ typedef enum {
   /* Needs host_seq_lens. The batch's (sequence, KV head) segments, each cut
    * into granules of G tokens (G = the wave tile, or the page if larger), are
    * laid end to end and cut into N near-equal ranges, one per workgroup
-   * (N = min(CUs x resident workgroups per CU, or CUs x wgs_per_cu when the
-   * caller sets it, and cdiv(total granules, 4))). A segment crossing a range
+   * (N = min(CUs x resident workgroups per CU (at most 2), or CUs x
+   * wgs_per_cu when the caller sets it, and cdiv(total granules, 4))). A segment crossing a range
    * boundary yields one state per range: a Stream-K-style partition of the
    * kind kanthi.in §7 lists (LeanAttention) against wave quantization, here
    * so that every workgroup streams the same number of bytes. */

@@ -169,7 +169,7 @@ def test_balanced_schedule_matches_oracle(paged):
     rng = np.random.default_rng(29)
     for trial in range(80):
         B = int(rng.choice([1, 2, 5, 16, 64]))
-        Hkv, g = ((8, 8), (8, 4), (2, 2), (4, 2))[trial % 4]
+        Hkv, g = ((8, 8), (8, 4), (2, 2), (4, 2), (8, 1))[trial % 5]
         lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(0, int(rng.choice([40, 2048, 40000])), B)]
         L = max(lens + [1])
         cus = int(rng.choice([7, 64, 256]))
@@ -198,11 +198,11 @@ def test_schedule_selection():
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=[3000] * 3).schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens).schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens, schedule="balanced").schedule == fd.SCHEDULES["balanced"]
-    # the VALU kernel has no balanced variant: AUTO falls back, an explicit request fails
+    # the VALU kernel (MHA) has its balanced variant too
     mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=3000)
-    assert fd.fd_plan(mha, num_cus=256, host_seq_lens=lens).schedule == fd.SCHEDULES["uniform"]
-    with pytest.raises(fd.FdError):
-        fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, schedule="balanced")
+    p = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens)
+    assert p.kernel == fd.KERNELS["valu"] and p.schedule == fd.SCHEDULES["balanced"]
+    assert p.slots == 512                               # two resident balanced workgroups per CU at most
     with pytest.raises(fd.FdError):
         fd.fd_plan(prob, num_cus=256, schedule="balanced")            # needs host lengths
     with pytest.raises(fd.FdError):

@@ -34,6 +34,18 @@ def case(name):
     if name == "one_long":
         return W.contiguous(name, seed=94, batch=1, q_heads=32, kv_heads=4, head_dim=128, capacity=20000,
                             seq_lens=[20000], dtype="bf16")
+    if name == "mha_f16_ragged":                 # VALU kernel (g = 1)
+        return W.contiguous(name, seed=99, batch=6, q_heads=8, kv_heads=8, head_dim=128, capacity=5000,
+                            seq_lens=[5000, 0, 17, 3100, 1, 900], dtype="f16")
+    if name == "mha_bf16_d64_qblock":            # VALU kernel, short query block (R = 2)
+        return W.contiguous(name, seed=100, batch=4, q_heads=4, kv_heads=4, head_dim=64, capacity=2500,
+                            seq_lens=[2500, 3, 0, 1200], dtype="bf16", q_len=2)
+    if name == "f32_g2":                         # VALU kernel, fp32 cache, g = 2
+        return W.contiguous(name, seed=101, batch=3, q_heads=8, kv_heads=4, head_dim=64, capacity=1500,
+                            seq_lens=[1500, 40, 700], dtype="f32")
+    if name == "paged_mha":
+        return W.paged(name, seed=102, batch=4, q_heads=8, kv_heads=8, head_dim=128,
+                       seq_lens=[3000, 16, 0, 1700], page_size=32, dtype="f16")
     if name.startswith("paged"):
         _, page, layout = name.split("_")
         return W.paged(name, seed=95, batch=5, q_heads=32, kv_heads=8, head_dim=128,
@@ -43,7 +55,7 @@ def case(name):
 
 
 CASES = ["gqa8_f16_ragged", "gqa4_bf16_d64", "gqa2_f16_many_tiny", "all_empty", "one_long",
-         "paged_16_hnd", "paged_64_nhd"]
+         "paged_16_hnd", "paged_64_nhd", "mha_f16_ragged", "mha_bf16_d64_qblock", "f32_g2", "paged_mha"]
 
 
 @pytest.mark.parametrize("cus", [256, 5])
@@ -56,7 +68,7 @@ def test_balanced_matches_oracle(name, cus):
 
 
 @pytest.mark.parametrize("ws_format", ["uml", "olse"])
-@pytest.mark.parametrize("name", ["gqa8_f16_ragged", "paged_16_hnd"])
+@pytest.mark.parametrize("name", ["gqa8_f16_ragged", "paged_16_hnd", "mha_f16_ragged"])
 def test_balanced_partial_states(name, ws_format):
     """Slot i of segment (b, h) holds the state of its i-th piece; slots past
     the segment's piece count hold the neutral state."""
@@ -86,7 +98,8 @@ def test_balanced_partial_states(name, ws_format):
 
 
 @pytest.mark.parametrize("cus", [256, 5])
-@pytest.mark.parametrize("name", ["gqa8_f16_ragged", "gqa2_f16_many_tiny", "all_empty", "paged_16_hnd"])
+@pytest.mark.parametrize("name", ["gqa8_f16_ragged", "gqa2_f16_many_tiny", "all_empty", "paged_16_hnd",
+                                  "mha_f16_ragged", "f32_g2"])
 def test_balanced_fused(name, cus):
     w = case(name)
     plan, out, lse, ctr = H.run_fused(w, num_cus=cus, schedule="balanced")
