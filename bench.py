@@ -166,6 +166,7 @@ def main():
     ap.add_argument("--schedule", choices=["auto", "uniform", "balanced"], default="auto",
                     help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner slots per CU (0 = library default)")
+    ap.add_argument("--kernel", choices=["auto", "mfma", "valu"], default="auto", help="split kernel (auto: planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
@@ -211,6 +212,8 @@ def main():
         opts["schedule"] = args.schedule
     if args.wgs_per_cu:
         opts["wgs_per_cu"] = args.wgs_per_cu
+    if args.kernel != "auto":
+        opts["kernel"] = args.kernel
     prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
     t0 = time.perf_counter()
     plan = fd.fd_plan(prob, **opts)

@@ -95,3 +95,15 @@ def test_edge_gqa_forced_masked_splits():
     M, Lw, U = A.split_states(H.cache_of(w), 8, 256, pairs=[(b, 0)])
     assert abs(m_s[b, 0, s] - M[b, 0, s]) < 1e-5 * max(1, abs(M[b, 0, s]))
     assert abs(l_s[b, 0, s] - 1.0) < 1e-6
+
+
+def test_max_length_single_sequence():
+    """One sequence of 2^20 tokens (one KV head, 8 query heads, D=128, fp16:
+    512 MiB of K/V) through the planner's default plan."""
+    L = 1 << 20
+    w = W.contiguous("max_len_1M", seed=7, batch=1, q_heads=8, kv_heads=1, head_dim=128, capacity=L,
+                     seq_lens=[L], dtype="f16")
+    plan, out, lse, _, _ = H.run(w)
+    H.say(f"1M-token plan: S={plan.num_splits} chunk={plan.chunk_tokens} schedule={plan.schedule}")
+    _finite_everywhere(out, lse, w.seq_lens)
+    H.check_against_oracle(w, out, lse, [(0, 0), (0, 5)])
