@@ -1,14 +1,17 @@
 // Split kernel, packed-GQA tile on MFMA (gfx950), 16-bit K/V.
 //
-// One workgroup of 4 waves owns one (sequence b, KV head, split s) and the g
-// query heads that share the KV head ("Flash-Decoding: Split-KV Attention for
-// Long-Context Decode", kanthi.in, §1 GQA note: the query heads of a group are
-// the rows of one tile so each KV block is read once per group). The split is
-// [s*chunk, min(s*chunk + chunk, seq_len)) (§4 kernel 1). Its 32-token wave
-// tiles are dealt round-robin to the 4 waves; each wave runs its own fp32
-// online softmax (§4 kernel 1 loop; the recurrence of Milakov & Gimelshein)
-// with no barrier inside the loop, and the four wave states are merged once
-// at the end with the exact rescaled merge (§2 stable form).
+// One workgroup of 4 waves processes a piece of one (sequence b, KV head)
+// segment for the g query heads that share the KV head, times the q_len rows
+// of a short query block ("Flash-Decoding: Split-KV Attention for Long-Context
+// Decode", kanthi.in, §1 GQA note: the query heads of a group are the rows of
+// one tile so each KV block is read once per group; §7 short query blocks).
+// Under the uniform schedule the piece is split s, [s*chunk, min(s*chunk +
+// chunk, seq_len)) (§4 kernel 1); under the balanced schedule (balance.h) a
+// workgroup walks the pieces of its equal share of the batch. A piece's
+// 32-token wave tiles are dealt round-robin to the 4 waves; each wave runs its
+// own fp32 online softmax (§4 kernel 1 loop; the recurrence of Milakov &
+// Gimelshein) with no barrier inside the loop, and the four wave states are
+// merged once at the end with the exact rescaled merge (§2 stable form).
 //
 // Per wave tile of 32 tokens:
 //   * K and V rows are fetched with fully coalesced 16-byte nontemporal loads
@@ -20,8 +23,10 @@
 //     bytes so the 16 rows one MFMA operand read touches fall in distinct bank
 //     groups, while every LDS access is one base register plus an immediate.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 tokens x 32 dims of
-//     K, B = 32 dims x 16 query columns. Columns 0..g-1 hold the g query heads;
-//     columns g..2g-1 hold the same heads again; the rest are zero.
+//     K, B = 32 dims x 16 query columns. Columns 0..R-1 hold the R = g * q_len
+//     query rows (column c: block row c / g, head c % g); columns R..2R-1 hold
+//     the same rows again; the rest are zero. Each column masks the tokens its
+//     block row may not see.
 //   * Online softmax in base 2: x = (q.k) * scale * log2(e); the running max
 //     is exchanged across the four 16-lane groups; p = 2^(x - m).
 //   * O^T += V^T P^T on the same MFMA: the S^T accumulator layout is already
@@ -30,7 +35,7 @@
 //     registers. On the V side each lane reads one contiguous D/8-byte slice
 //     of a token row; output block e then holds dims d = (D/16)*m + e, so one
 //     read feeds all D/16 MFMAs. P is split into a 16-bit high part (columns
-//     < g) and the 16-bit rounding of its remainder (columns g..2g-1); the two
+//     < R) and the 16-bit rounding of its remainder (columns R..2R-1); the two
 //     output columns are summed at the end, so P keeps ~22 (f16) / ~16 (bf16)
 //     bits. The row sum l is accumulated from the unrounded fp32 p.
 #include <hip/hip_runtime.h>

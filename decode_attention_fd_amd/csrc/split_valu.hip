@@ -1,5 +1,8 @@
-// Split kernel on the vector ALUs: one (sequence, KV head, split) per
-// workgroup of 4 waves, for MHA (g = 1), small groups (g <= 4) and fp32 caches.
+// Split kernel on the vector ALUs: a piece of one (sequence, KV head) segment
+// per workgroup of 4 waves (one split under the uniform schedule, a walk over
+// an equal share under the balanced one, balance.h), for MHA (g = 1), small
+// groups and fp32 caches; the R = g * q_len query rows (<= 4) of a group are
+// the kernel's rows, each masking the tokens its block row may not see.
 //
 // A K/V row of D elements is spread over LPR lanes, 16 bytes per lane, so one
 // wave load instruction reads RPI = 64 / LPR whole rows (coalesced). Each lane
