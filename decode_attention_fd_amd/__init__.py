@@ -53,7 +53,8 @@ class PlanOpts(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32), ("force_splits", ctypes.c_int32),
         ("force_chunk_tokens", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("kernel", ctypes.c_int32),
         ("heuristic", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("overhead_budget", ctypes.c_float),
-        ("num_host_seq_lens", ctypes.c_int32), ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
+        ("num_host_seq_lens", ctypes.c_int32), ("schedule", ctypes.c_int32), ("piece_cost_tokens", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
         ("host_seq_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
@@ -65,6 +66,7 @@ class Plan(ctypes.Structure):
         ("tile_tokens", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("slots", ctypes.c_int32),
         ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
         ("scale", ctypes.c_float), ("schedule", ctypes.c_int32),
+        ("piece_cost", ctypes.c_int32), ("reserved2", ctypes.c_int32),
         ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64), ("ws_counter_bytes", ctypes.c_int64),
         ("prob", Problem), ("checksum", ctypes.c_uint64),
     ]
@@ -199,7 +201,7 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: tor
 def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_splits: int = 0,
             force_chunk_tokens: int = 0, ws_format: str = "uml", kernel: str = "auto",
             heuristic: str = "mi355x", max_splits: int = 0, overhead_budget: float = 0.0,
-            host_seq_lens=None, schedule: str = "auto") -> Plan:
+            host_seq_lens=None, schedule: str = "auto", piece_cost_tokens: int = 0) -> Plan:
     """Call ``fd_plan``. ``num_cus=0`` asks the current device. ``host_seq_lens``
     (a host list / CPU tensor of the batch's lengths) enables length-aware
     splits and the balanced schedule."""
@@ -217,6 +219,7 @@ def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_sp
     o.max_splits = max_splits
     o.overhead_budget = overhead_budget
     o.schedule = SCHEDULES[schedule]
+    o.piece_cost_tokens = piece_cost_tokens
     plan = Plan()
     _check(lib().fd_plan(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(plan)), "fd_plan")
     del keep

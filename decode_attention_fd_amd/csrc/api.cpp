@@ -100,7 +100,7 @@ int check_plan(const fd_plan_t* plan) {
   if (validate_problem(&plan->prob) != FD_OK) return FD_ERR_BAD_PLAN;
   if (plan->num_splits < 1 || plan->chunk_tokens < 1) return FD_ERR_BAD_PLAN;
   if (plan->schedule != FD_SCHEDULE_UNIFORM && plan->schedule != FD_SCHEDULE_BALANCED) return FD_ERR_BAD_PLAN;
-  if (plan->schedule == FD_SCHEDULE_BALANCED && plan->grid_x < 1) return FD_ERR_BAD_PLAN;
+  if (plan->schedule == FD_SCHEDULE_BALANCED && (plan->grid_x < 1 || plan->piece_cost < 0)) return FD_ERR_BAD_PLAN;
   return FD_OK;
 }
 
@@ -235,6 +235,7 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
   if (plan->schedule == FD_SCHEDULE_BALANCED) {
     p.nwg = plan->grid_x;
     p.granule = plan->chunk_tokens;
+    p.piece_cost = plan->piece_cost;
   } else {
     // Tokens past S*chunk belong to no split: clamp there as well.
     const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;

@@ -9,7 +9,10 @@
 // "Flash-Decoding: Split-KV Attention for Long-Context Decode", kanthi.in, §7).
 //
 // Here the whole batch is one line of granules: segment (b, h) is
-// cdiv(len_b, G) granules of G tokens, segments in (b, h) order. A grid of N
+// cdiv(len_b, G) granules of G tokens followed by piece_cost granules that
+// hold no tokens and stand for a piece's start-up cost (q load, first-tile
+// latency, epilogue), so a range of many short segments gets fewer tokens;
+// segments are in (b, h) order. A grid of N
 // workgroups cuts that line into N near-equal ranges, workgroup w taking
 // granules [floor(w T / N), floor((w + 1) T / N)) of the T in total. A range
 // may cover the end of one segment and the start of the next; each part of a
@@ -119,6 +122,7 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   const int B = p.B;
   const int64_t G = p.granule;
   const int64_t H = p.Hkv;
+  const int64_t C = p.piece_cost;
   const int E = (B + NTHREADS - 1) / NTHREADS;
   const int r0 = threadIdx.x * E;
   const int r1 = min(B, r0 + E);
@@ -126,7 +130,8 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   for (int r = r0; r < r1; ++r) {
     const int n = clamp_len(p, r);
     if (E == 1) sh.len[threadIdx.x] = n;
-    local += H * ((n + G - 1) / G);
+    const int64_t pl = (n + G - 1) / G;
+    local += H * (pl > 0 ? pl + C : 0);
   }
 
   // inclusive scan inside the wave, then across the waves
@@ -155,7 +160,8 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   int cand = B;
   int64_t cand_x = 0;
   for (int r = r0; r < r1; ++r) {
-    const int64_t xn = x + H * ((clamp_len(p, r) + G - 1) / G);
+    const int64_t pl = (clamp_len(p, r) + G - 1) / G;
+    const int64_t xn = x + H * (pl > 0 ? pl + C : 0);
     if (x >= gs || xn > gs) {
       cand = r;
       cand_x = x;
@@ -209,11 +215,13 @@ __device__ __forceinline__ void balanced_walk(const SplitParams& p, Piece&& piec
       empty_row(b);
       continue;
     }
-    const int h0 = x >= st.gs ? 0 : (int)((st.gs - x) / plen);
+    const int64_t slen = plen + p.piece_cost;           // the segment's place on the line
+    const int h0 = x >= st.gs ? 0 : (int)((st.gs - x) / slen);
     for (int h = h0; h < p.Hkv; ++h) {
-      const int64_t ss = x + h * plen;
-      const int64_t se = ss + plen;
+      const int64_t ss = x + h * slen;
+      const int64_t se = ss + plen;                      // end of its token granules
       if (ss >= st.ge) break;
+      if (se <= st.gs) continue;                         // only its cost granules fall in this range
       const int64_t ps = ss > st.gs ? ss : st.gs;
       const int64_t pe = se < st.ge ? se : st.ge;
       const int64_t first = granule_owner(ss, st.total, nwg);
@@ -222,7 +230,7 @@ __device__ __forceinline__ void balanced_walk(const SplitParams& p, Piece&& piec
       const int64_t t1 = (pe - ss) * G;
       piece(b, h, (int)((ps - ss) * G), (int)(t1 < len ? t1 : len), slot, count, se <= st.ge, len);
     }
-    x += p.Hkv * plen;
+    x += p.Hkv * slen;
   }
 }
 

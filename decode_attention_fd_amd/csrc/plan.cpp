@@ -154,6 +154,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   if (o->ws_format != FD_WS_UML && o->ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
   if (o->heuristic != FD_HEURISTIC_MI355X && o->heuristic != FD_HEURISTIC_FA2) return FD_ERR_INVALID_ARG;
   if (!(o->overhead_budget >= 0.0f)) return FD_ERR_INVALID_ARG;
+  if (o->piece_cost_tokens < -1 || o->piece_cost_tokens > (1 << 20)) return FD_ERR_INVALID_ARG;
   if (o->num_host_seq_lens < 0 || (o->num_host_seq_lens > 0 && !o->host_seq_lens)) return FD_ERR_INVALID_ARG;
   if (o->num_host_seq_lens > 0 && o->num_host_seq_lens != prob->batch) return FD_ERR_INVALID_ARG;
   if (o->schedule < FD_SCHEDULE_AUTO || o->schedule > FD_SCHEDULE_BALANCED) return FD_ERR_INVALID_ARG;
@@ -183,11 +184,13 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   int64_t S = 1, chunk = 1;
   int64_t slots = 0;
   int64_t nwg = 0;                      // balanced grid (0: uniform)
+  int64_t piece_cost = 0;               // balanced: cost granules per non-empty segment
   // AUTO takes the balanced schedule where it pays: ragged lengths (equal
   // lengths are already balanced by the uniform chunks) and no more segments
-  // than workgroup slots (a workgroup then meets about two segments; with
-  // many short segments per workgroup the pieces' start-up latencies, paid
-  // one after another, cost more than the balance gains).
+  // than workgroup slots. With more segments than slots the uniform grid
+  // already has a workgroup per segment, often a single split that the fused
+  // call writes directly, and balanced pieces would add a merge (64-sequence
+  // edge batch: 58 us uniform one-split vs 61 us balanced plus merge).
   bool ragged = false;
   for (int b = 1; b < o->num_host_seq_lens; ++b) ragged |= o->host_seq_lens[b] != o->host_seq_lens[0];
   const bool balanced =
@@ -205,10 +208,16 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
       slots = (int64_t)o->num_cus * (balanced_wgs_per_cu > 0 ? balanced_wgs_per_cu : o->wgs_per_cu);
       const int64_t G = tile > paged_align ? tile : paged_align;
       const int64_t H = prob->num_kv_heads;
+      // Default start-up cost of a piece: 256 tokens (sweep on ragged batches:
+      // none 92 us, 128 tokens 62 us, 256 tokens 55 us, 512 tokens 57 us on the
+      // 64-sequence edge batch).
+      const int64_t cost_tok = o->piece_cost_tokens > 0 ? o->piece_cost_tokens : (o->piece_cost_tokens < 0 ? 0 : 256);
+      piece_cost = cdiv64(cost_tok, G);
+      auto seg_len = [&](int64_t plen) { return plen > 0 ? plen + piece_cost : 0; };
       int64_t T = 0;
       for (int b = 0; b < prob->batch; ++b) {
         const int32_t n = o->host_seq_lens[b] > 0 ? o->host_seq_lens[b] : 0;
-        T += H * cdiv64(n, G);
+        T += H * seg_len(cdiv64(n, G));
       }
       nwg = T > 0 ? cdiv64(T, 4) : 1;
       if (nwg > slots) nwg = slots;
@@ -220,11 +229,11 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
         const int32_t n = o->host_seq_lens[b] > 0 ? o->host_seq_lens[b] : 0;
         const int64_t plen = cdiv64(n, G);
         for (int64_t h = 0; h < H && plen > 0; ++h) {
-          const int64_t ss = x + h * plen;
+          const int64_t ss = x + h * seg_len(plen);
           const int64_t c = owner(ss + plen - 1) - owner(ss) + 1;
           if (c > S) S = c;
         }
-        x += H * plen;
+        x += H * seg_len(plen);
       }
       chunk = G;
     }
@@ -296,6 +305,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   out->waves_per_wg = waves;
   out->slots = (int32_t)slots;
   out->schedule = nwg > 0 ? FD_SCHEDULE_BALANCED : FD_SCHEDULE_UNIFORM;
+  out->piece_cost = (int32_t)piece_cost;
   out->grid_x = nwg > 0 ? (int32_t)nwg : (int32_t)S;
   out->grid_y = nwg > 0 ? 1 : prob->num_kv_heads;
   out->grid_z = nwg > 0 ? 1 : prob->batch;

@@ -112,7 +112,9 @@ typedef enum {
   FD_SCHEDULE_UNIFORM = 1,
   /* Needs host_seq_lens. The batch's (sequence, KV head) segments, each cut
    * into granules of G tokens (G = the wave tile, or the page if larger), are
-   * laid end to end and cut into N near-equal ranges, one per workgroup
+   * laid end to end, each followed by a few granules that stand for the
+   * start-up cost of a piece (q load, first tile, epilogue; no tokens), and
+   * cut into N near-equal ranges, one per workgroup
    * (N = min(CUs x resident workgroups per CU (at most 2), or CUs x
    * wgs_per_cu when the caller sets it, and cdiv(total granules, 4))). A segment crossing a range
    * boundary yields one state per range: a Stream-K-style partition of the
@@ -174,7 +176,9 @@ typedef struct {
   float overhead_budget;      /* 0: 0.02 (workspace bytes <= 2% of KV bytes) */
   int32_t num_host_seq_lens;  /* entries in host_seq_lens (0: none; else must equal batch) */
   int32_t schedule;           /* fd_schedule */
-  int32_t reserved[5];
+  int32_t piece_cost_tokens;  /* balanced schedule: start-up cost of one piece, in KV tokens, added
+                                 to every non-empty segment when the line is cut (0: 256; -1: none) */
+  int32_t reserved[4];
   /* Optional HOST copy of seq_lens (int32 [batch]). With it the MI355X rule
    * sizes splits from the batch's total work: no split longer than one
    * slot's share, cdiv(Hkv * sum(len), slots) tokens, so a ragged batch is
@@ -200,6 +204,8 @@ typedef struct {
   int32_t schedule;           /* fd_schedule actually used (UNIFORM or BALANCED). BALANCED:
                                  chunk_tokens is the granule G, grid (N, 1, 1), and S is the
                                  largest number of pieces any (b, kv head) segment is cut into */
+  int32_t piece_cost;         /* BALANCED: granules of start-up cost added per non-empty segment */
+  int32_t reserved2;
   int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
   int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
   int64_t ws_counter_bytes;   /* uint32 [B, Hkv] arrival counters of fd_decode_fused */

@@ -112,34 +112,38 @@ def chunk_from_lengths(lengths, max_len: int, kv_heads: int, slots: int, align: 
         chunk += align
 
 
-def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_granules: int = 4):
+def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_granules: int = 4, cost: int = 0):
     """The balanced split schedule, from its definition: segment (b, h) is
-    cdiv(len_b, G) granules; the segments, in (b, h) order, form one line of T
-    granules; N = min(slots, cdiv(T, min_granules)) workgroups (1 if T = 0)
-    take the ranges [floor(w T / N), floor((w + 1) T / N)). Every non-empty
-    intersection of a range with a segment is one piece. Returns
-    (N, S, pieces) with pieces[(b, h)] = [(w, token_lo, token_hi), ...] in
+    cdiv(len_b, G) token granules followed by ``cost`` granules that hold no
+    tokens (a piece's start-up cost; none for an empty segment); the
+    segments, in (b, h) order, form one line of T granules; N = min(slots,
+    cdiv(T, min_granules)) workgroups (1 if T = 0) take the ranges
+    [floor(w T / N), floor((w + 1) T / N)). Every non-empty intersection of a
+    range with a segment's token granules is one piece. Returns (N, S,
+    pieces, T) with pieces[(b, h)] = [(w, token_lo, token_hi), ...] in
     workgroup order and S = the largest number of pieces of one segment (at
     least 1). It is a Stream-K-style partition of the kind kanthi.in §7 lists
-    (LeanAttention), one that gives every workgroup the same bytes.
-    Parity unpinned as a performance choice; its partition is checked
-    exhaustively in tests."""
+    (LeanAttention), one that gives every workgroup the same bytes plus
+    start-up costs. Parity unpinned as a performance choice; its partition is
+    checked exhaustively in tests."""
     lens = [max(0, int(n)) for n in lengths]
     plens = [cdiv(n, granule) for n in lens]
-    T = kv_heads * sum(plens)
+    seg = [p + cost if p > 0 else 0 for p in plens]
+    T = kv_heads * sum(seg)
     N = min(slots, cdiv(T, min_granules)) if T > 0 else 1
     ranges = [(w * T // N, (w + 1) * T // N) for w in range(N)]
     pieces = {}
     x = 0
-    for b, (n, plen) in enumerate(zip(lens, plens)):
+    for b, (n, plen, sl) in enumerate(zip(lens, plens, seg)):
         for h in range(kv_heads):
-            ss, se = x + h * plen, x + (h + 1) * plen
+            ss = x + h * sl
+            se = ss + plen
             lst = []
             for w, (gs, ge) in enumerate(ranges):
                 lo, hi = max(ss, gs), min(se, ge)
                 if lo < hi:
                     lst.append((w, (lo - ss) * granule, min((hi - ss) * granule, n)))
             pieces[(b, h)] = lst
-        x += kv_heads * plen
+        x += kv_heads * sl
     S = max([1] + [len(v) for v in pieces.values()])
-    return N, S, pieces
+    return N, S, pieces, T

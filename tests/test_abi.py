@@ -180,7 +180,8 @@ def test_balanced_schedule_matches_oracle(paged):
         assert plan.schedule == fd.SCHEDULES["balanced"]
         G = max(32, page)
         assert plan.slots == cus * 2                   # two resident D=128 16-bit workgroups per CU
-        N, S, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots)
+        assert plan.piece_cost == -(-256 // G)           # default start-up cost: 256 tokens
+        N, S, _, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots, cost=plan.piece_cost)
         assert (plan.grid_x, plan.grid_y, plan.grid_z) == (N, 1, 1), (lens, cus)
         assert plan.num_splits == S and plan.chunk_tokens == G
         assert plan.ws_o_bytes == B * Hkv * g * S * 128 * 4
@@ -196,8 +197,11 @@ def test_schedule_selection():
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, heuristic="fa2").schedule == fd.SCHEDULES["uniform"]
     # equal lengths, or more segments than slots: uniform
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=[3000] * 3).schedule == fd.SCHEDULES["uniform"]
-    assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens).schedule == fd.SCHEDULES["uniform"]
-    assert fd.fd_plan(prob, num_cus=2, host_seq_lens=lens, schedule="balanced").schedule == fd.SCHEDULES["balanced"]
+    many = contiguous_problem(B=40, Hq=32, Hkv=8, L=3000)                   # 320 segments > 256 slots
+    many_lens = [3000 - (i % 7) for i in range(40)]
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=many_lens).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=many_lens,
+                      schedule="balanced").schedule == fd.SCHEDULES["balanced"]
     # the VALU kernel (MHA) has its balanced variant too
     mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=3000)
     p = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens)

@@ -77,7 +77,7 @@ def test_balanced_partial_states(name, ws_format):
     plan, out, lse, ws_o, ws_stats = H.run(w, num_cus=cus, ws_format=ws_format, schedule="balanced")
     assert plan.schedule == BAL
     lens = w.seq_lens.tolist()
-    N, S, pieces = OP.balanced_schedule(lens, w.num_kv_heads, plan.chunk_tokens, plan.slots)
+    N, S, pieces, _ = OP.balanced_schedule(lens, w.num_kv_heads, plan.chunk_tokens, plan.slots, cost=plan.piece_cost)
     assert (plan.grid_x, plan.num_splits) == (N, S)
     B, Hq = w.batch, w.num_q_heads
     M, Lw, U = A.split_states(H.cache_of(w), S, plan.chunk_tokens,
@@ -113,7 +113,7 @@ def test_balanced_equals_uniform_bitwise_when_pieces_coincide():
     the uniform splits, so the two schedules give identical bits."""
     w = W.contiguous("coincide", seed=96, batch=1, q_heads=64, kv_heads=8, head_dim=128, capacity=32000,
                      seq_lens=[32000], dtype="f16")
-    p1, o1, l1, _, _ = H.run(w, num_cus=64, wgs_per_cu=1, schedule="balanced")
+    p1, o1, l1, _, _ = H.run(w, num_cus=64, wgs_per_cu=1, schedule="balanced", piece_cost_tokens=-1)
     p2, o2, l2, _, _ = H.run(w, num_cus=64, schedule="uniform", host_seq_lens=None, force_chunk_tokens=4000)
     assert (p1.grid_x, p1.num_splits) == (64, 8) and p2.num_splits == 8
     assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -71,8 +71,8 @@ def test_balanced_schedule_partitions_every_segment():
         G = int(rng.choice([16, 32, 64]))
         lens = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(0, int(rng.choice([5, 300, 5000])), B)]
         slots = int(rng.choice([1, 3, 7, 64, 256]))
-        N, S, pieces = P.balanced_schedule(lens, hkv, G, slots)
-        T = hkv * sum(-(-n // G) for n in lens)
+        N, S, pieces, T = P.balanced_schedule(lens, hkv, G, slots)
+        assert T == hkv * sum(-(-n // G) for n in lens)
         assert 1 <= N <= max(1, min(slots, T))
         share = [0] * N
         for (b, h), lst in pieces.items():
@@ -90,3 +90,34 @@ def test_balanced_schedule_partitions_every_segment():
         assert sum(share) == T
         if T:
             assert max(share) - min(share) <= 1
+
+
+def test_balanced_schedule_with_piece_cost():
+    """With start-up cost granules on the line, pieces still tile every
+    segment exactly; the line holds the cost of every non-empty segment; and
+    a workgroup whose range covers many short segments receives fewer tokens
+    than one covering a single long segment."""
+    import numpy as np
+    rng = np.random.default_rng(4)
+    for trial in range(100):
+        B = int(rng.integers(1, 20))
+        hkv, G, cost = int(rng.choice([1, 4])), 32, int(rng.choice([1, 4, 8]))
+        lens = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(0, 3000, B)]
+        N, S, pieces, T = P.balanced_schedule(lens, hkv, G, int(rng.choice([3, 64, 256])), cost=cost)
+        assert T == hkv * sum(-(-n // G) + cost for n in lens if n > 0)
+        for (b, h), lst in pieces.items():
+            n = lens[b]
+            if n == 0:
+                assert lst == []
+                continue
+            assert lst[0][1] == 0 and lst[-1][2] == n
+            for (w0, _, hi0), (w1, lo1, _) in zip(lst, lst[1:]):
+                assert hi0 == lo1 and w1 > w0
+    lens = [32] * 12 + [32 * 120]                # twelve 1-granule rows, then a long one
+    N, S, pieces, T = P.balanced_schedule(lens, 1, 32, 2, cost=4)
+    assert N == 2
+    tokens = [0, 0]
+    for lst in pieces.values():
+        for w, lo, hi in lst:
+            tokens[w] += hi - lo
+    assert tokens[0] < tokens[1]
