@@ -222,6 +222,15 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
       nwg = T > 0 ? cdiv64(T, 4) : 1;
       if (nwg > slots) nwg = slots;
       if (nwg > 0x7fffffff) return FD_ERR_UNSUPPORTED;
+      // The kernels rebuild the line from the device lengths (clamped to the
+      // capacity) and form products of granule positions with the grid size
+      // in 64 bits: bound the longest line any device lengths could give.
+      {
+        const int64_t cap = prob->layout == FD_LAYOUT_PAGED ? (int64_t)prob->max_pages_per_seq * prob->page_size
+                                                            : (int64_t)prob->kv_capacity;
+        const int64_t t_max = (int64_t)prob->batch * H * (cdiv64(cap, G) + piece_cost);
+        if (t_max > ((int64_t)1 << 62) / (nwg + 1)) return FD_ERR_UNSUPPORTED;
+      }
       auto owner = [&](int64_t x) { return ((x + 1) * nwg + T - 1) / T - 1; };
       S = 1;
       int64_t x = 0;
