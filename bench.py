@@ -55,6 +55,34 @@ def make_workload(name: str, device):
     return builders[name]()
 
 
+def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0, kernel: str = "auto") -> dict:
+    """fd_plan options of a benchmark run: the workload's forced splits or
+    chunk if it has them, else the planner fed the host copy of the lengths."""
+    opts = {"ws_format": w.ws_format}
+    if splits:
+        opts["force_splits"] = splits
+    elif w.num_splits:
+        opts["force_splits"] = w.num_splits
+    if w.chunk_tokens and not splits:
+        opts["force_chunk_tokens"] = w.chunk_tokens
+    if "force_splits" not in opts and "force_chunk_tokens" not in opts:
+        opts["host_seq_lens"] = w.seq_lens.cpu().tolist()   # length-aware split plan
+        opts["schedule"] = schedule
+    if wgs_per_cu:
+        opts["wgs_per_cu"] = wgs_per_cu
+    if kernel != "auto":
+        opts["kernel"] = kernel
+    return opts
+
+
+def choose_path(plan, path: str = "auto") -> str:
+    """auto: the fused call when the plan has one split (its rows are written
+    directly), else split + merge."""
+    if path != "auto":
+        return path
+    return "fused" if plan.num_splits == 1 else "split"
+
+
 def kernel_source_hash() -> str:
     """Hash of the sources the MFMA split kernel is compiled from (the kernel
     the roofline and the traffic record describe)."""
@@ -200,20 +228,7 @@ def main():
     ws = [w0] + [W.redraw_kv(w0, 7000 + i) for i in range(1, copies)]
     torch.cuda.synchronize()
 
-    opts = {"ws_format": w0.ws_format}
-    if args.splits:
-        opts["force_splits"] = args.splits
-    elif w0.num_splits:
-        opts["force_splits"] = w0.num_splits
-    if w0.chunk_tokens and not args.splits:
-        opts["force_chunk_tokens"] = w0.chunk_tokens
-    if "force_splits" not in opts and "force_chunk_tokens" not in opts:
-        opts["host_seq_lens"] = w0.seq_lens.cpu().tolist()   # length-aware split plan
-        opts["schedule"] = args.schedule
-    if args.wgs_per_cu:
-        opts["wgs_per_cu"] = args.wgs_per_cu
-    if args.kernel != "auto":
-        opts["kernel"] = args.kernel
+    opts = plan_options(w0, args.splits, args.schedule, args.wgs_per_cu, args.kernel)
     prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
     t0 = time.perf_counter()
     plan = fd.fd_plan(prob, **opts)
@@ -223,7 +238,7 @@ def main():
     out = torch.empty(w0.batch, w0.num_q_heads, w0.head_dim, dtype=torch.float32, device=dev)
     lse = torch.empty(w0.batch, w0.num_q_heads, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    path = args.path if args.path != "auto" else ("fused" if plan.num_splits == 1 else "split")
+    path = choose_path(plan, args.path)
 
     def step(i, evs=None):
         w = ws[i % copies]

@@ -107,3 +107,28 @@ def test_max_length_single_sequence():
     H.say(f"1M-token plan: S={plan.num_splits} chunk={plan.chunk_tokens} schedule={plan.schedule}")
     _finite_everywhere(out, lse, w.seq_lens)
     H.check_against_oracle(w, out, lse, [(0, 0), (0, 5)])
+
+
+@pytest.mark.parametrize("name", ["gqa64x8_f16_L128000", "mha32_bf16_L65536_C1024", "paged_gqa32x8_f16_B16",
+                                  "edge_gqa32x8_f16_B64", "tiny_mha_f32_L1000"])
+def test_bench_launch_configuration(name):
+    """The benchmark's own plan options and path choice (bench.plan_options,
+    bench.choose_path) at full size, checked on sampled rows."""
+    import bench
+
+    w = bench.make_workload(name, "cpu")
+    opts = bench.plan_options(w)
+    dev = torch.device("cuda", 0)
+    prob = fd.problem_for(w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev),
+                          None if w.block_table is None else w.block_table.to(dev), max_seq_len=w.max_seq_len)
+    plan = fd.fd_plan(prob, **opts)
+    path = bench.choose_path(plan)
+    H.say(f"{name}: S={plan.num_splits} schedule={plan.schedule} kernel={plan.kernel} path={path}")
+    if path == "fused":
+        plan2, out, lse, ctr = H.run_fused(w, **opts)
+        assert torch.all(ctr == 0).item()
+    else:
+        plan2, out, lse, _, _ = H.run(w, **opts)
+    assert (plan2.num_splits, plan2.chunk_tokens, plan2.schedule) == (plan.num_splits, plan.chunk_tokens, plan.schedule)
+    _finite_everywhere(out, lse, w.seq_lens)
+    H.check_against_oracle(w, out, lse, H.sample_pairs(w.batch, w.num_q_heads, 16, seed=11))
