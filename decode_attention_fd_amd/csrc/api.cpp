@@ -13,12 +13,13 @@
 namespace fd {
 
 int valu_tile_tokens(int head_dim, int kv_dtype);          // split_valu.hip
-int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int* out);
+int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int nct, int* out);
 int occupancy_split_valu(int head_dim, int kv_dtype, int layout, int group_tpl, int* out);
 
-int occupancy_split(int kernel, int head_dim, int kv_dtype, int layout, int group_tpl, int* out) {
-  if (kernel == FD_KERNEL_MFMA) return occupancy_split_mfma(head_dim, kv_dtype, layout, out);
-  return occupancy_split_valu(head_dim, kv_dtype, layout, group_tpl, out);
+// `variant`: MFMA column tiles (1 or 2) or the VALU row template (1, 2, 4).
+int occupancy_split(int kernel, int head_dim, int kv_dtype, int layout, int variant, int* out) {
+  if (kernel == FD_KERNEL_MFMA) return occupancy_split_mfma(head_dim, kv_dtype, layout, variant, out);
+  return occupancy_split_valu(head_dim, kv_dtype, layout, variant, out);
 }
 
 int split_tile_tokens(int kernel, int head_dim, int kv_dtype) {
@@ -44,7 +45,7 @@ int default_wgs_per_cu(int kernel, int head_dim, int kv_dtype, int group_tpl, in
   const int paged = layout == FD_LAYOUT_PAGED;
   for (const OccRow& r : kOccupancy)
     if (r.kernel == kernel && r.head_dim == head_dim && r.kv_dtype == kv_dtype && r.paged == paged &&
-        (kernel == FD_KERNEL_MFMA || r.group_tpl == group_tpl))
+        r.group_tpl == group_tpl)
       return r.wgs;
   return 1;
 }
@@ -154,7 +155,8 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   if (st != FD_OK) return st;
   const int kernel = choose_kernel(prob, o.kernel);
   if (kernel < 0) return -kernel;
-  const int gtpl = valu_group_template(prob->num_q_heads / prob->num_kv_heads * (prob->q_len > 1 ? prob->q_len : 1));
+  const int rows = prob->num_q_heads / prob->num_kv_heads * (prob->q_len > 1 ? prob->q_len : 1);
+  const int gtpl = kernel == FD_KERNEL_MFMA ? (rows > 8 ? 2 : 1) : valu_group_template(rows);
   // Resident split workgroups per CU: the device's answer when we query it,
   // else the table generated from the compiler's resource usage.
   int resident = 0;

@@ -161,27 +161,31 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   if (!s_last) return;
 
   constexpr int LPR = D / 4;
-  const int g = p.R;                          // rows of the group
-  const int SG = 1 << split_groups_log2(p.S, LPR, g, NTHREADS);
-  const int tpr = LPR * SG;
-  const int h = threadIdx.x / tpr;
-  const int t = threadIdx.x - h * tpr;
-  const int grp = t / LPR;
-  const int dl = t - grp * LPR;
-  const bool active = h < g;
+  constexpr int ROWS_PER_PASS = NTHREADS / LPR;
   const bool uml = p.ws_format == FD_WS_UML;
-  const int64_t row = state_row(p, b, kvh, active ? h : 0);
+  for (int r0 = 0; r0 < p.R; r0 += ROWS_PER_PASS) {       // the group's rows, a block of them at a time
+    const int g = p.R - r0 < ROWS_PER_PASS ? p.R - r0 : ROWS_PER_PASS;
+    const int SG = 1 << split_groups_log2(p.S, LPR, g, NTHREADS);
+    const int tpr = LPR * SG;
+    const int h = threadIdx.x / tpr;
+    const int t = threadIdx.x - h * tpr;
+    const int grp = t / LPR;
+    const int dl = t - grp * LPR;
+    const bool active = h < g;
+    const int64_t row = state_row(p, b, kvh, r0 + (active ? h : 0));
 
-  RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
-  if (active)
-    st = fold_splits_coherent<D>(p.ws_o + row * p.S * D + dl * 4, p.ws_stats + row * p.S * (uml ? 2 : 1), p.S, uml,
-                                 grp, SG);
-  part[threadIdx.x] = st.acc;
-  part_m[threadIdx.x] = st.m;
-  part_d[threadIdx.x] = st.den;
-  __syncthreads();
-  if (active && grp == 0)
-    finish_row(part, part_m, part_d, h * tpr + dl, LPR, SG, p.out + row * D, dl, p.lse ? p.lse + row : nullptr);
+    RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
+    if (active)
+      st = fold_splits_coherent<D>(p.ws_o + row * p.S * D + dl * 4, p.ws_stats + row * p.S * (uml ? 2 : 1), p.S,
+                                   uml, grp, SG);
+    if (r0 > 0) __syncthreads();                           // the previous block's reads of part[] are done
+    part[threadIdx.x] = st.acc;
+    part_m[threadIdx.x] = st.m;
+    part_d[threadIdx.x] = st.den;
+    __syncthreads();
+    if (active && grp == 0)
+      finish_row(part, part_m, part_d, h * tpr + dl, LPR, SG, p.out + row * D, dl, p.lse ? p.lse + row : nullptr);
+  }
   if (threadIdx.x == 0)
     __hip_atomic_store(p.counters + (int64_t)b * p.Hkv + kvh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -116,7 +116,7 @@ int choose_kernel(const fd_problem* p, int requested) {
   // g = query rows one KV head serves: the group's heads times the block's queries.
   const int g = p->num_q_heads / p->num_kv_heads * (p->q_len > 1 ? p->q_len : 1);
   const bool half = dtype_size(p->kv_dtype) == 2;
-  const bool mfma_ok = half && g <= 8;
+  const bool mfma_ok = half && g <= 16;          // one or two 8-row column tiles
   const bool valu_ok = valu_group_template(g) != 0;
   switch (requested) {
     case FD_KERNEL_AUTO:

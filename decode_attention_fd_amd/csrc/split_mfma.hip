@@ -97,16 +97,19 @@ __device__ __forceinline__ unsigned pick_half(unsigned a, unsigned b, int e) {
 
 template <int D> struct Smem {
   unsigned char lds[NW][2][Geo<D>::TILEB];
-  float st_m[NW][16];
-  float st_l[NW][16];
+  float st_m[NW][32];
+  float st_l[NW][32];
 };
 
 // Tokens [start, end) of segment (b, kvh), end > start, for the R = g * q_len
-// query rows of the group (MFMA column c: block row c / g, head c % g); the
-// state goes to split slot `slot`, or, with `direct` (the segment's only
-// piece, fused call), straight to out/lse as the finished rows. Block row i
-// sees tokens below vis0 + i (vis0 = seq_len - (q_len - 1)).
-template <int D, typename T, bool PAGED>
+// query rows of the group (row r: block row r / g, head r % g); the state goes
+// to split slot `slot`, or, with `direct` (the segment's only piece, fused
+// call), straight to out/lse as the finished rows. Block row i sees tokens
+// below vis0 + i (vis0 = seq_len - (q_len - 1)). NCT column tiles of the MFMA
+// B operand: with NCT = 1 columns 0..R-1 hold rows 0..R-1 (R <= 8); with
+// NCT = 2 tile ct holds rows 8*ct .. 8*ct + 7 (R <= 16). Within a tile of RT
+// rows, columns RT..2RT-1 repeat them for the low half of P.
+template <int D, typename T, bool PAGED, int NCT>
 __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, int b, int kvh, int start, int end,
                                             int slot, int vis0, bool direct) {
   using G = Geo<D>;
@@ -124,20 +127,24 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
   const int grp = lane >> 4;     // 16-lane group
   const int ntiles = (end - start + TT - 1) / TT;
 
-  // ---- Q^T as the B operand of S^T = K Q^T: column col holds head h(col).
-  const int hcol = col < R ? col : (col < 2 * R ? col - R : -1);
-  const int qi = hcol < 0 ? p.q_len - 1 : hcol / g;          // block row of this column
-  const int col_end = min(end, vis0 + qi);                    // first token this column may not see
+  // ---- Q^T as the B operand of S^T = K Q^T, one column tile at a time.
   const int mask_from = min(end, vis0);                       // first token any column may not see
-  V8 qb[G::NDC];
-  {
-    const int hh = hcol < 0 ? 0 : hcol - qi * g;
+  int RT[NCT];                                                // rows of tile ct
+  int col_end[NCT];                                           // first token column col of tile ct may not see
+  V8 qb[NCT][G::NDC];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    RT[ct] = NCT == 1 ? R : min(8, R - 8 * ct);
+    const int hc = col < RT[ct] ? col : (col < 2 * RT[ct] ? col - RT[ct] : -1);
+    const int r = hc < 0 ? R - 1 : 8 * ct + hc;              // state row of this column
+    const int qi = r / g;                                     // its block row
+    col_end[ct] = min(end, vis0 + qi);
     const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t)b * p.q_sb + (int64_t)qi * p.q_sq +
-                    (int64_t)(kvh * g + hh) * p.q_sh;
+                    (int64_t)(kvh * g + r - qi * g) * p.q_sh;
 #pragma unroll
     for (int c = 0; c < G::NDC; ++c) {
       V8 v = *reinterpret_cast<const V8*>(qrow + 32 * c + 8 * grp);
-      qb[c] = hcol < 0 ? V8{} : v;
+      qb[ct][c] = hc < 0 ? V8{} : v;
     }
   }
 
@@ -205,15 +212,22 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       *reinterpret_cast<u32x4*>(dst + (i * G::RPI + lrow) * G::ROWP + lchunk * 16) = r[i];
   };
 
-  f32x4 oacc[G::NDB];
+  f32x4 oacc[NCT][G::NDB];
+  float m_run[NCT];          // running max of x (base-2 scaled scores) for column col of tile ct
+  float l_run[NCT];          // this lane's share of the running sum
 #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of x (base-2 scaled scores) for column col
-  float l_run = 0.f;         // this lane's share of the running sum
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int i = 0; i < G::NDB; ++i) oacc[ct][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
   const float c2 = p.scale_log2;
 
   // One tile from the wave's LDS slice into the running state.
   auto compute = [&](int t0) {
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
     // ---- S^T = K Q^T for tokens [0,16) and [16,32)
     f32x4 sacc[2];
 #pragma unroll
@@ -222,7 +236,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
 #pragma unroll
       for (int c = 0; c < G::NDC; ++c) {
         V8 a = *reinterpret_cast<const V8*>(ldsK + (tb * 16 + col) * G::ROWP + (4 * c + grp) * 16);
-        sacc[tb] = Mma<T>::run(a, qb[c], sacc[tb]);
+        sacc[tb] = Mma<T>::run(a, qb[ct][c], sacc[tb]);
       }
     }
 
@@ -237,7 +251,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + tb * 16 + 4 * grp + i >= col_end) x[tb * 4 + i] = -INFINITY;
+          if (t0 + tb * 16 + 4 * grp + i >= col_end[ct]) x[tb * 4 + i] = -INFINITY;
     }
     float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -245,15 +259,15 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
     // A column of a query block can see no token of a tile (its max stays
     // -inf): the rescale and the exponent then use safe references, so
     // e^(-inf - (-inf)) is never formed.
-    const float m_new = fmaxf(m_run, mt);
-    if (__any(m_new > m_run)) {
-      const float alpha = m_new > m_run ? exp2_fast(m_run - m_new) : 1.f;
-      l_run *= alpha;
+    const float m_new = fmaxf(m_run[ct], mt);
+    if (__any(m_new > m_run[ct])) {
+      const float alpha = m_new > m_run[ct] ? exp2_fast(m_run[ct] - m_new) : 1.f;
+      l_run[ct] *= alpha;
 #pragma unroll
-      for (int i = 0; i < G::NDB; ++i) oacc[i] *= alpha;
-      m_run = m_new;
+      for (int i = 0; i < G::NDB; ++i) oacc[ct][i] *= alpha;
+      m_run[ct] = m_new;
     }
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    const float m_ref = m_run[ct] == -INFINITY ? 0.f : m_run[ct];
     float pe[8];
     float psum = 0.f;
 #pragma unroll
@@ -261,14 +275,14 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       pe[e] = exp2_fast(x[e] - m_ref);
       psum += pe[e];
     }
-    l_run += psum;
+    l_run[ct] += psum;
 
-    // ---- P^T as the B operand: high part in columns < R, remainder after.
+    // ---- P^T as the B operand: high part in columns < RT, remainder after.
     V8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const T hi = (T)pe[e];
-      const float r = col < R ? pe[e] : pe[e] - (float)hi;
+      const float r = col < RT[ct] ? pe[e] : pe[e] - (float)hi;
       pb[e] = (T)r;
     }
 
@@ -286,8 +300,9 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       u32x4 a;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) a[jj] = pick_half(w[2 * jj][e >> 1], w[2 * jj + 1][e >> 1], e);
-      oacc[e] = Mma<T>::run(__builtin_bit_cast(V8, a), pb, oacc[e]);
+      oacc[ct][e] = Mma<T>::run(__builtin_bit_cast(V8, a), pb, oacc[ct][e]);
     }
+  }
   };
 
   // One register tile per tensor, staggered: the K tile is stored and the next
@@ -318,40 +333,48 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
     }
   }
 
-  // ---- per-wave state -> LDS: ow[column][d], d = NDB*(4*grp + i) + e
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  float* ow = reinterpret_cast<float*>(lds[wave][0]);   // [16 columns][D] fp32 (<= TILEB bytes)
+  // ---- per-wave state -> LDS: tile ct in lds[wave][ct] as ow[column][d],
+  // d = NDB*(4*grp + i) + e; statistics at st_m/st_l[wave][16*ct + column]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int ct = 0; ct < NCT; ++ct) {
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    float* ow = reinterpret_cast<float*>(lds[wave][ct]);   // [16 columns][D] fp32 (<= TILEB bytes)
 #pragma unroll
-    for (int e4 = 0; e4 < G::NDB; e4 += 4) {
-      f32x4 v = {oacc[e4][i], oacc[e4 + 1][i], oacc[e4 + 2][i], oacc[e4 + 3][i]};
-      *reinterpret_cast<f32x4*>(ow + col * D + G::NDB * (4 * grp + i) + e4) = v;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < G::NDB; e4 += 4) {
+        f32x4 v = {oacc[ct][e4][i], oacc[ct][e4 + 1][i], oacc[ct][e4 + 2][i], oacc[ct][e4 + 3][i]};
+        *reinterpret_cast<f32x4*>(ow + col * D + G::NDB * (4 * grp + i) + e4) = v;
+      }
+    if (grp == 0) {
+      st_m[wave][16 * ct + col] = m_run[ct];
+      st_l[wave][16 * ct + col] = l;
     }
-  if (grp == 0) {
-    st_m[wave][col] = m_run;
-    st_l[wave][col] = l_run;
   }
   __syncthreads();
 
   // ---- merge the four wave states (exact rescale to the common max) and
   // combine the high/low columns, then write the split's state.
   for (int idx = threadIdx.x; idx < R * D; idx += NW * 64) {
-    const int h = idx / D;
+    const int h = idx / D;                     // state row
     const int d = idx - h * D;
+    const int ct = NCT == 1 ? 0 : h >> 3;      // its column tile
+    const int c = NCT == 1 ? h : h & 7;        // and column
+    const int rt = NCT == 1 ? R : min(8, R - 8 * ct);
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, st_m[w2][h]);
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, st_m[w2][16 * ct + c]);
     float U = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) {
-        const float mw = st_m[w2][h];
+        const float mw = st_m[w2][16 * ct + c];
         const float a = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
-        const float* o = reinterpret_cast<const float*>(lds[w2][0]);
-        U += a * (o[h * D + d] + o[(h + R) * D + d]);
-        L += a * st_l[w2][h];
+        const float* o = reinterpret_cast<const float*>(lds[w2][ct]);
+        U += a * (o[c * D + d] + o[(c + rt) * D + d]);
+        L += a * st_l[w2][16 * ct + c];
       }
     }
     const int64_t row = state_row(p, b, kvh, h);
@@ -376,7 +399,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
 }
 
 // Uniform schedule: workgroup (s, kvh, b) owns split s of segment (b, kvh).
-template <int D, typename T, bool PAGED>
+template <int D, typename T, bool PAGED, int NCT>
 __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   __shared__ Smem<D> sm;
   const int s = blockIdx.x;
@@ -388,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   const int end = min(start + p.chunk, seq_len);
   const bool direct = p.fused && p.S == 1;
   if (end > start)
-    split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
+    split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
   else if (direct)
     empty_group<D, NW * 64>(p, b, kvh);
   else
@@ -397,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
 }
 
 // Balanced schedule: workgroup w owns an equal share of the batch's granules.
-template <int D, typename T, bool PAGED>
+template <int D, typename T, bool PAGED, int NCT>
 __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParams p) {
   __shared__ Smem<D> sm;
   balanced_walk<NW * 64>(
@@ -410,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
         slot = __builtin_amdgcn_readfirstlane(slot);
         if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
         const bool direct = p.fused && count == 1;
-        split_piece<D, T, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
+        split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
         if (!direct) {
           if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
           if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
@@ -421,18 +444,26 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
 }
 
 template <int D, typename T, bool PAGED>
-int occupancy(int* out) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, split_mfma_kernel<D, T, PAGED>, NW * 64, 0);
+int occupancy(int nct, int* out) {
+  if (nct == 2)
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, split_mfma_kernel<D, T, PAGED, 2>, NW * 64, 0);
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, split_mfma_kernel<D, T, PAGED, 1>, NW * 64, 0);
+}
+
+template <int D, typename T, bool PAGED, int NCT>
+int launch_nct(const SplitParams& p, hipStream_t st) {
+  if (p.nwg > 0)
+    hipLaunchKernelGGL((split_mfma_balanced_kernel<D, T, PAGED, NCT>), dim3(p.nwg), dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((split_mfma_kernel<D, T, PAGED, NCT>), dim3(p.S, p.Hkv, p.B), dim3(NW * 64), 0, st, p);
+  return (int)hipGetLastError();
 }
 
 template <int D, typename T, bool PAGED>
 int launch(const SplitParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (p.nwg > 0)
-    hipLaunchKernelGGL((split_mfma_balanced_kernel<D, T, PAGED>), dim3(p.nwg), dim3(NW * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((split_mfma_kernel<D, T, PAGED>), dim3(p.S, p.Hkv, p.B), dim3(NW * 64), 0, st, p);
-  return (int)hipGetLastError();
+  if (p.R > 16) return (int)hipErrorInvalidValue;
+  return p.R > 8 ? launch_nct<D, T, PAGED, 2>(p, st) : launch_nct<D, T, PAGED, 1>(p, st);
 }
 
 }  // namespace
@@ -449,14 +480,15 @@ int launch_split_mfma(const SplitParams& p, int head_dim, int kv_dtype, int layo
   return (int)hipErrorInvalidValue;
 }
 
-int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int* out) {
+// Resident workgroups per CU of the uniform kernel with nct column tiles.
+int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int nct, int* out) {
   const bool paged = layout == FD_LAYOUT_PAGED;
   if (kv_dtype == FD_DTYPE_F16) {
-    if (head_dim == 128) return paged ? occupancy<128, _Float16, true>(out) : occupancy<128, _Float16, false>(out);
-    if (head_dim == 64) return paged ? occupancy<64, _Float16, true>(out) : occupancy<64, _Float16, false>(out);
+    if (head_dim == 128) return paged ? occupancy<128, _Float16, true>(nct, out) : occupancy<128, _Float16, false>(nct, out);
+    if (head_dim == 64) return paged ? occupancy<64, _Float16, true>(nct, out) : occupancy<64, _Float16, false>(nct, out);
   } else if (kv_dtype == FD_DTYPE_BF16) {
-    if (head_dim == 128) return paged ? occupancy<128, __bf16, true>(out) : occupancy<128, __bf16, false>(out);
-    if (head_dim == 64) return paged ? occupancy<64, __bf16, true>(out) : occupancy<64, __bf16, false>(out);
+    if (head_dim == 128) return paged ? occupancy<128, __bf16, true>(nct, out) : occupancy<128, __bf16, false>(nct, out);
+    if (head_dim == 64) return paged ? occupancy<64, __bf16, true>(nct, out) : occupancy<64, __bf16, false>(nct, out);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -154,7 +154,8 @@ typedef struct {
    * of each sequence, whose K/V are already in the cache: query row i sees
    * tokens [0, seq_len - (q_len - 1 - i)) (each query keeps its own
    * visibility, xuujii §06); a row that sees nothing gets O = 0, LSE = -inf.
-   * Needs g * q_len <= 8 (MFMA kernel, 16-bit caches) or <= 4 (VALU kernel).
+   * Needs g * q_len <= 16 (MFMA kernel, 16-bit caches; one 8-row column tile
+   * up to 8 rows, two beyond) or <= 4 (VALU kernel).
    * out and lse gain the same row axis: [B, q_len, Hq, D] and [B, q_len, Hq];
    * the workspace holds B * q_len * Hq rows. */
   int32_t q_len;          /* query rows per sequence; 0 or 1: a single query */

@@ -257,7 +257,7 @@ def test_problem_validation():
     assert _status(paged_problem(L=1000, max_pages_per_seq=10)) == fd.FD_ERR_INVALID_ARG
     assert _status(paged_problem(), force_chunk_tokens=40) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(Hq=64, Hkv=8, dtype=0)) == fd.FD_ERR_UNSUPPORTED    # fp32, g = 8
-    assert _status(contiguous_problem(Hq=128, Hkv=8)) == fd.FD_ERR_UNSUPPORTED            # g = 16
+    assert _status(contiguous_problem(Hq=256, Hkv=8)) == fd.FD_ERR_UNSUPPORTED            # g = 32
     assert _status(contiguous_problem(dtype=0), kernel="mfma") == fd.FD_ERR_UNSUPPORTED
     assert _status(contiguous_problem(L=1000), force_chunk_tokens=100, force_splits=5) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(scale=float("nan"))) == fd.FD_ERR_INVALID_ARG
@@ -345,8 +345,9 @@ def test_query_block_problems():
         p.q_stride_b = q_len * Hq * 128
         return p
     assert fd.fd_plan(qb(4), num_cus=256).kernel == fd.KERNELS["mfma"]          # g=2, R=8
+    assert fd.fd_plan(qb(8), num_cus=256).kernel == fd.KERNELS["mfma"]          # R=16: two column tiles
     with pytest.raises(fd.FdError):
-        fd.fd_plan(qb(5), num_cus=256)                                          # R=10 > 8
+        fd.fd_plan(qb(5, Hq=16, Hkv=4), num_cus=256)                             # g=4, R=20 > 16
     assert fd.fd_plan(qb(8, Hq=4, Hkv=4), num_cus=256, kernel="mfma").kernel == fd.KERNELS["mfma"]
     assert fd.fd_plan(qb(2, Hq=4, Hkv=4, dtype=0), num_cus=256).kernel == fd.KERNELS["valu"]   # fp32: VALU
     with pytest.raises(fd.FdError):

@@ -25,7 +25,8 @@ def block(g, q_len, dtype, lens=LENS, seed=0, paged=False, D=128):
                         capacity=max(lens), seq_lens=lens, dtype=dtype, q_len=q_len)
 
 
-MFMA_CASES = [(1, 2, "f16"), (1, 8, "bf16"), (2, 4, "f16"), (4, 2, "bf16"), (2, 3, "f16"), (8, 1, "f16")]
+MFMA_CASES = [(1, 2, "f16"), (1, 8, "bf16"), (2, 4, "f16"), (4, 2, "bf16"), (2, 3, "f16"), (8, 1, "f16"),
+              (8, 2, "f16"), (4, 3, "bf16"), (3, 3, "f16"), (2, 8, "bf16")]     # last four: two column tiles
 VALU_CASES = [(1, 4, "f32"), (2, 2, "bf16"), (1, 3, "f16"), (4, 1, "f32")]
 
 
@@ -100,3 +101,16 @@ def test_block_of_one_equals_single_query():
     p1, o1, l1, _, _ = H.run(w, force_splits=3)
     p2, o2, l2, _, _ = H.run(w4, force_splits=3)
     assert torch.equal(o1, o2.squeeze(1)) and torch.equal(l1, l2.squeeze(1))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_two_column_tiles_fused_and_balanced(D):
+    """g = 8 with a 2-row block (16 rows per KV head, two MFMA column tiles)
+    through the fused merge and the balanced schedule."""
+    w = block(8, 2, "bf16", lens=[2600, 1, 0, 1800], seed=8, D=D)
+    plan, out, lse, ctr = H.run_fused(w, num_cus=7, schedule="balanced")
+    assert plan.schedule == fd.SCHEDULES["balanced"] and torch.all(ctr == 0).item()
+    H.check_against_oracle(w, out, lse)
+    plan, out, lse, ctr = H.run_fused(w, force_splits=4, host_seq_lens=None)
+    assert torch.all(ctr == 0).item()
+    H.check_against_oracle(w, out, lse)

@@ -24,7 +24,7 @@ def config(i):
         g = int(rng.choice([1, 2, 3, 4, 8]))
         q_len = int(rng.choice([1, 1, 2, 3, 4]))
         R = g * q_len
-        if (half and R <= 8) or R <= 4:
+        if (half and R <= 16) or R <= 4:
             break
     Hkv = int(rng.choice([1, 2, 3]))
     B = int(rng.choice([1, 2, 5]))
