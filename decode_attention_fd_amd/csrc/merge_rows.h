@@ -3,28 +3,41 @@
 // ("Flash-Decoding: Split-KV Attention for Long-Context Decode", kanthi.in,
 // §2 stable form; xuujii KB "Decode 专项 Attention" §04).
 //
-// A row of D floats is read by D/4 lanes (16 bytes each). SG groups of such
-// lanes share the row's splits (split s goes to group s % SG); each lane folds
-// its splits in one pass, rebasing its running sums whenever a larger maximum
-// arrives, and the SG partial states are then merged through LDS the same way.
-// A split whose m (lse) is -inf weighs exactly 0; a row whose splits are all
-// empty gives O = 0 and LSE = -inf. Every sum has a fixed order.
+// Two forms. The merge kernel gives each row SG groups of D/4 lanes and folds
+// split by split (its many workgroups keep the memory system busy). The fused
+// tail, where one workgroup merges a whole group of rows, needs more loads in
+// flight per lane: there one wave (or WPR waves) merges one row. Lane (grp, dl) covers dims
+// [4 dl, 4 dl + 4) (D/4 lanes per group) of splits grp, grp + NG, ... where NG
+// is the number of lane groups on the row. A lane issues the loads of
+// NB of its splits together and folds the batch into its running
+// state with one rescale to the larger maximum, so a row of S splits costs
+// about S / (NG * NB) memory round trips. The lane groups are then
+// combined by cross-lane shuffles and, with WPR > 1, through LDS. A split
+// whose m (lse) is -inf weighs exactly 0; a row whose splits are all empty
+// gives O = 0 and LSE = -inf. Every sum has a fixed order.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdint.h>
 
 #include "fd.h"
 
 namespace fd {
 
 typedef float mf32x4 __attribute__((ext_vector_type(4)));
+typedef float mf32x2 __attribute__((ext_vector_type(2)));
 
 struct RowState {
   mf32x4 acc;
   float m;
   float den;
 };
+
+// ---- merge kernel (split states of a finished launch): SG groups of D/4 lanes
+// share a row's splits (split s goes to group s % SG); each lane folds its
+// splits one at a time, rebasing its running sums whenever a larger maximum
+// arrives, and the SG partial states are then merged through LDS.
 
 // Fold splits grp, grp + SG, ... of one row. `stats` points at the row's first
 // split statistic, `ws` at the row's first split vector plus this lane's dims.
@@ -45,8 +58,8 @@ __device__ __forceinline__ RowState fold_splits(const float* __restrict__ ws, co
     const float mn = valid ? fmaxf(st.m, ms) : st.m;
     const float a = st.m == -INFINITY ? 0.f : expf(st.m - mn);
     const float w = valid ? expf(ms - mn) : 0.f;
-    st.acc = st.acc * a + u * w;
-    st.den = st.den * a + ls * w;
+    st.acc = st.acc * a + (valid ? u * w : mf32x4{0.f, 0.f, 0.f, 0.f});
+    st.den = st.den * a + (valid ? ls * w : 0.f);
     st.m = mn;
   }
   return st;
@@ -81,6 +94,172 @@ __host__ __device__ inline int split_groups_log2(int S, int lanes_per_row, int r
   return sg;
 }
 
+// ---- fused tail (states published in the same launch): one or more waves per row.
+
+
+// Cache policy bits of the state loads. COHERENT (sc1) is the form the
+// compiler gives agent-scope atomic loads on gfx950: it reads states that
+// other workgroups of the same launch published with device-coherent stores.
+constexpr int LOAD_PLAIN = 0;
+constexpr int LOAD_COHERENT = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The same pointer, marked wave-uniform (a buffer resource lives in SGPRs).
+__device__ __forceinline__ const float* uniform_ptr(const float* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
+}
+
+// Fold splits gi, gi + NG, ... of one row into a lane state. ws_row and st_row
+// (wave-uniform) are the row's first split vector and statistic.
+// NB: splits whose loads one lane has in flight together.
+template <int D, bool UML, int POLICY, int NB>
+__device__ __forceinline__ RowState fold_row(const float* ws_row, const float* st_row, int S, int gi, int NG, int dl) {
+  constexpr int SW = UML ? 2 : 1;
+  const __amdgpu_buffer_rsrc_t ru = row_rsrc(ws_row, (uint32_t)S * D * 4);
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(st_row, (uint32_t)S * SW * 4);
+  RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
+  for (int s0 = gi; s0 < S; s0 += NB * NG) {
+    mf32x4 u[NB];
+    float m[NB], l[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int s = s0 + j * NG;
+      u[j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+      if (s < S) {                              // issued back to back; first used after the batch
+        u[j] = __builtin_bit_cast(mf32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, (uint32_t)(s * D + 4 * dl) * 4,
+                                                                              0, POLICY));
+        if (UML) {
+          const mf32x2 ml =
+              __builtin_bit_cast(mf32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)s * 8, 0, POLICY));
+          m[j] = ml.x;
+          l[j] = ml.y;
+        } else {
+          m[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)s * 4, 0, POLICY));
+          l[j] = 1.f;
+        }
+      }
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bm = fmaxf(bm, m[j]);
+    if (bm == -INFINITY) continue;
+    const float mn = fmaxf(st.m, bm);
+    const float a = st.m == -INFINITY ? 0.f : expf(st.m - mn);
+    st.acc = st.acc * a;
+    st.den = st.den * a;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bool valid = m[j] != -INFINITY;
+      const float w = valid ? expf(m[j] - mn) : 0.f;
+      st.acc += valid ? u[j] * w : mf32x4{0.f, 0.f, 0.f, 0.f};
+      st.den += valid ? l[j] * w : 0.f;
+    }
+    st.m = mn;
+  }
+  return st;
+}
+
+// a <- merge(a, b), both rescaled to the larger maximum.
+__device__ __forceinline__ void combine(RowState& a, const RowState& b) {
+  const float M = fmaxf(a.m, b.m);
+  const float wa = a.m == -INFINITY ? 0.f : expf(a.m - M);
+  const float wb = b.m == -INFINITY ? 0.f : expf(b.m - M);
+  a.acc = a.acc * wa + b.acc * wb;
+  a.den = a.den * wa + b.den * wb;
+  a.m = M;
+}
+
+// Combine the lane groups of a wave (lanes dl, dl + LPR, ...): afterwards
+// every lane holds the state of its dims over all of the wave's splits.
+template <int LPR>
+__device__ __forceinline__ RowState wave_combine(RowState st) {
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    RowState o;
+    o.m = __shfl_xor(st.m, off);
+    o.den = __shfl_xor(st.den, off);
+    o.acc = mf32x4{__shfl_xor(st.acc.x, off), __shfl_xor(st.acc.y, off), __shfl_xor(st.acc.z, off),
+                   __shfl_xor(st.acc.w, off)};
+    combine(st, o);
+  }
+  return st;
+}
+
+// Final O = acc / den (4 floats at out_row + 4 dl) and, for dl == 0, LSE.
+__device__ __forceinline__ void write_row(const RowState& st, float* out_row, float* lse, int dl) {
+  const bool empty = !(st.den > 0.f);
+  const float inv = empty ? 0.f : 1.f / st.den;
+  *reinterpret_cast<mf32x4*>(out_row + 4 * dl) = st.acc * inv;
+  if (lse && dl == 0) *lse = empty ? -INFINITY : st.m + logf(st.den);
+}
+
+template <int NW> struct MergeLds {
+  mf32x4 acc[NW][32];
+  float m[NW];
+  float den[NW];
+};
+
+// Waves per row (log2) for `rows` rows on NW waves: the most that still
+// merges every row in one pass, at least one.
+__host__ __device__ inline int waves_per_row_log2(int rows, int nw) {
+  int w = 0;
+  while ((2 << w) <= nw && rows * (2 << w) <= nw) ++w;
+  return w;
+}
+
+// One pass of the workgroup over NW >> wpr_log2 rows: waves [k WPR, k WPR + WPR)
+// merge state row `row` (wave-uniform; `active` false for a wave without a row).
+// Every thread of the workgroup calls it; with wpr_log2 > 0 it holds barriers.
+template <int D, int NW, int POLICY, int NB>
+__device__ __forceinline__ void merge_row_pass(int64_t row, bool active, int S, bool uml, int wpr_log2,
+                                               const float* ws_o, const float* ws_stats, float* out, float* lse,
+                                               MergeLds<NW>& sh) {
+  constexpr int LPR = D / 4;
+  constexpr int SGW = 64 / LPR;                // lane groups per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wsub = wave & ((1 << wpr_log2) - 1);
+  const int grp = lane / LPR;
+  const int dl = lane - grp * LPR;
+  RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
+  if (active) {
+    const float* wr = uniform_ptr(ws_o + row * S * D);
+    const float* sr = uniform_ptr(ws_stats + row * S * (uml ? 2 : 1));
+    const int NG = SGW << wpr_log2;
+    const int gi = wsub * SGW + grp;
+    st = uml ? fold_row<D, true, POLICY, NB>(wr, sr, S, gi, NG, dl) : fold_row<D, false, POLICY, NB>(wr, sr, S, gi, NG, dl);
+    st = wave_combine<LPR>(st);
+  }
+  if (wpr_log2 == 0) {
+    if (active && grp == 0) write_row(st, out + row * D, lse ? lse + row : nullptr, dl);
+    return;
+  }
+  if (grp == 0) {
+    sh.acc[wave][dl] = st.acc;
+    if (dl == 0) {
+      sh.m[wave] = st.m;
+      sh.den[wave] = st.den;
+    }
+  }
+  __syncthreads();
+  if (active && wsub == 0 && grp == 0) {
+    for (int k = 1; k < (1 << wpr_log2); ++k) {
+      const RowState o = {sh.acc[wave + k][dl], sh.m[wave + k], sh.den[wave + k]};
+      combine(st, o);
+    }
+    write_row(st, out + row * D, lse ? lse + row : nullptr, dl);
+  }
+  __syncthreads();
+}
+
 }  // namespace fd
 
 #include "fd_internal.h"
@@ -105,51 +284,18 @@ __device__ __forceinline__ void ws_store(float* p, float v, bool coherent) {
     *p = v;
 }
 
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// fold_splits for states published in the same launch: device-coherent loads,
-// eight splits in flight per lane.
-template <int D>
-__device__ __forceinline__ RowState fold_splits_coherent(const float* ws, const float* stats, int S, bool uml,
-                                                         int grp, int SG) {
-  const int sstride = uml ? 2 : 1;
-  RowState st;
-  st.acc = mf32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.den = 0.f;
-#pragma unroll 8
-  for (int s = grp; s < S; s += SG) {
-    const float ms = coherent_load(stats + s * sstride);
-    const float ls = uml ? coherent_load(stats + s * sstride + 1) : 1.f;
-    const float* u4 = ws + (int64_t)s * D;
-    const mf32x4 u = {coherent_load(u4), coherent_load(u4 + 1), coherent_load(u4 + 2), coherent_load(u4 + 3)};
-    const bool valid = ms != -INFINITY;
-    const float mn = valid ? fmaxf(st.m, ms) : st.m;
-    const float a = st.m == -INFINITY ? 0.f : expf(st.m - mn);
-    const float w = valid ? expf(ms - mn) : 0.f;
-    st.acc = st.acc * a + u * w;
-    st.den = st.den * a + ls * w;
-    st.m = mn;
-  }
-  return st;
-}
-
 // Fused merge at the end of a split workgroup (or of one piece of it) (the "last CTA merges" variant of
 // the kanthi.in chapter's decode contract). Every workgroup of a (sequence,
 // KV head) group has written its split states with ws_store(..., true); once
 // its own stores have completed (s_waitcnt) the workgroup counts itself in
 // with a device-scope atomic, and the one that arrives as number `expected`
 // (the group's writer count) reads the group's
-// states back with device-coherent loads, merges the g rows into out/lse and
-// resets the counter to 0 so the next stream-ordered call starts from zero.
-template <int D, int NTHREADS>
+// states back with device-coherent loads, merges the group's g * q_len rows
+// into out/lse and resets the counter to 0 so the next stream-ordered call
+// starts from zero.
+template <int D, int NTHREADS, int NB>
 __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, int kvh, int expected) {
   __shared__ int s_last;
-  __shared__ mf32x4 part[NTHREADS];
-  __shared__ float part_m[NTHREADS];
-  __shared__ float part_d[NTHREADS];
   __builtin_amdgcn_s_waitcnt(0);            // this thread's state stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -160,31 +306,16 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   __syncthreads();
   if (!s_last) return;
 
-  constexpr int LPR = D / 4;
-  constexpr int ROWS_PER_PASS = NTHREADS / LPR;
+  constexpr int NWV = NTHREADS / 64;
+  __shared__ MergeLds<NWV> sh;
   const bool uml = p.ws_format == FD_WS_UML;
-  for (int r0 = 0; r0 < p.R; r0 += ROWS_PER_PASS) {       // the group's rows, a block of them at a time
-    const int g = p.R - r0 < ROWS_PER_PASS ? p.R - r0 : ROWS_PER_PASS;
-    const int SG = 1 << split_groups_log2(p.S, LPR, g, NTHREADS);
-    const int tpr = LPR * SG;
-    const int h = threadIdx.x / tpr;
-    const int t = threadIdx.x - h * tpr;
-    const int grp = t / LPR;
-    const int dl = t - grp * LPR;
-    const bool active = h < g;
-    const int64_t row = state_row(p, b, kvh, r0 + (active ? h : 0));
-
-    RowState st = {mf32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
-    if (active)
-      st = fold_splits_coherent<D>(p.ws_o + row * p.S * D + dl * 4, p.ws_stats + row * p.S * (uml ? 2 : 1), p.S,
-                                   uml, grp, SG);
-    if (r0 > 0) __syncthreads();                           // the previous block's reads of part[] are done
-    part[threadIdx.x] = st.acc;
-    part_m[threadIdx.x] = st.m;
-    part_d[threadIdx.x] = st.den;
-    __syncthreads();
-    if (active && grp == 0)
-      finish_row(part, part_m, part_d, h * tpr + dl, LPR, SG, p.out + row * D, dl, p.lse ? p.lse + row : nullptr);
+  const int wpr_log2 = waves_per_row_log2(p.R, NWV);
+  const int per_pass = NWV >> wpr_log2;
+  const int k = (threadIdx.x >> 6) >> wpr_log2;
+  for (int r0 = 0; r0 < p.R; r0 += per_pass) {            // the group's rows, per_pass of them at a time
+    const bool active = r0 + k < p.R;
+    const int64_t row = state_row(p, b, kvh, active ? r0 + k : 0);
+    merge_row_pass<D, NWV, LOAD_COHERENT, NB>(row, active, p.S, uml, wpr_log2, p.ws_o, p.ws_stats, p.out, p.lse, sh);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(p.counters + (int64_t)b * p.Hkv + kvh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

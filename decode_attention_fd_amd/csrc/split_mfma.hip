@@ -69,6 +69,7 @@ template <> struct Mma<__bf16> {
 };
 
 constexpr int NW = 4;    // waves per workgroup
+constexpr int FUSED_BATCH = 16;   // splits per lane in flight in the fused merge
 constexpr int TT = 32;   // tokens per wave tile
 constexpr float LN2 = 0.69314718055994530942f;
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
     empty_group<D, NW * 64>(p, b, kvh);
   else
     write_neutral<D, NW * 64>(p, b, kvh, s, s + 1);
-  if (p.fused && !direct) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+  if (p.fused && !direct) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, p.S);
 }
 
 // Balanced schedule: workgroup w owns an equal share of the batch's granules.
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
         split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
         if (!direct) {
           if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
-          if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+          if (p.fused) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, count < p.S ? count : p.S);
         }
         __syncthreads();                         // LDS is reused by the next piece
       },

@@ -34,6 +34,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NW = 4;
+constexpr int FUSED_BATCH = 8;   // splits per lane in flight in the fused merge
 constexpr int U = 8;      // load instructions per tile per tensor
 constexpr float LN2 = 0.69314718055994530942f;
 
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int end = min(start + p.chunk, seq_len);
   const bool direct = p.fused && p.S == 1;    // fused call with one split: write out/lse directly
   valu_piece<D, T, G, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
-  if (p.fused && !direct) fused_group_merge<D, NW * 64>(p, b, kvh, p.S);
+  if (p.fused && !direct) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, p.S);
 }
 
 // Balanced schedule: workgroup w owns an equal share of the batch's granules.
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_balanced_kernel(SplitParam
         valu_piece<D, T, G, PAGED>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
         if (!direct) {
           if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
-          if (p.fused) fused_group_merge<D, NW * 64>(p, b, kvh, count < p.S ? count : p.S);
+          if (p.fused) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, count < p.S ? count : p.S);
         }
         __syncthreads();                         // LDS is reused by the next piece
       },
