@@ -77,10 +77,13 @@ def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0
 
 def choose_path(plan, path: str = "auto") -> str:
     """auto: the fused call when the plan has one split (its rows are written
-    directly), else split + merge."""
+    directly) or is balanced (its one-piece segments are written directly and
+    only the others are merged), else split + merge."""
+    import decode_attention_fd_amd as fd
+
     if path != "auto":
         return path
-    return "fused" if plan.num_splits == 1 else "split"
+    return "fused" if plan.num_splits == 1 or plan.schedule == fd.SCHEDULES["balanced"] else "split"
 
 
 def kernel_source_hash() -> str:
@@ -190,7 +193,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=64, help="(b, head) outputs the CPU oracle times")
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
                     help="fused: one launch (last workgroup per group merges); split: split + merge kernels; "
-                         "auto: fused when the plan has one split (the rows are written directly), else split")
+                         "auto: fused when the plan has one split or is balanced, else split")
     ap.add_argument("--schedule", choices=["auto", "uniform", "balanced"], default="auto",
                     help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner slots per CU (0 = library default)")

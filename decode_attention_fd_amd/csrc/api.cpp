@@ -171,11 +171,12 @@ FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* 
   // Workgroups per CU in one wave of the MI355X split rule: 1 by default (one
   // streaming split workgroup per CU saturates its share of HBM; measured by
   // split-count sweeps), never more than can be resident.
-  // The balanced kernels carry the walk's state on top of the split loop's and
+  // The balanced schedule takes one range per CU unless the caller asks for
+  // more; its kernels carry the walk's state on top of the split loop's and
   // keep two workgroups per CU resident at most.
   const int balanced_resident = resident < 2 ? resident : 2;
   const int balanced_wgs =
-      o.wgs_per_cu > 0 ? (o.wgs_per_cu < balanced_resident ? o.wgs_per_cu : balanced_resident) : balanced_resident;
+      o.wgs_per_cu > 0 ? (o.wgs_per_cu < balanced_resident ? o.wgs_per_cu : balanced_resident) : 1;
   if (o.wgs_per_cu == 0) o.wgs_per_cu = 1;
   if (o.wgs_per_cu > resident) o.wgs_per_cu = resident;
   o.kernel = kernel;

@@ -186,32 +186,42 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   int64_t nwg = 0;                      // balanced grid (0: uniform)
   int64_t piece_cost = 0;               // balanced: cost granules per non-empty segment
   // AUTO takes the balanced schedule where it pays: ragged lengths (equal
-  // lengths are already balanced by the uniform chunks) and no more segments
-  // than workgroup slots. With more segments than slots the uniform grid
-  // already has a workgroup per segment, often a single split that the fused
-  // call writes directly, and balanced pieces would add a merge (64-sequence
-  // edge batch: 58 us uniform one-split vs 61 us balanced plus merge).
+  // lengths are already balanced by the uniform chunks) whose mean is at
+  // least FD_BALANCED_MIN_MEAN_TOKENS. A balanced workgroup runs its pieces
+  // one after another, each with its own start-up and epilogue, while a
+  // uniform grid of many short workgroups has those overlapped by the
+  // hardware dispatcher: on ragged batches (lengths U[1, hi], one workgroup
+  // per CU) balanced was 3-35 % faster at mean lengths of 1000-2700 tokens,
+  // level at ~700 and 2-30 % slower at 250-500.
   bool ragged = false;
-  for (int b = 1; b < o->num_host_seq_lens; ++b) ragged |= o->host_seq_lens[b] != o->host_seq_lens[0];
+  int64_t len_sum = 0;
+  for (int b = 0; b < o->num_host_seq_lens; ++b) {
+    ragged |= o->host_seq_lens[b] != o->host_seq_lens[0];
+    len_sum += o->host_seq_lens[b] > 0 ? o->host_seq_lens[b] : 0;
+  }
+  const bool long_enough =
+      o->num_host_seq_lens > 0 && len_sum >= (int64_t)FD_BALANCED_MIN_MEAN_TOKENS * o->num_host_seq_lens;
   const bool balanced =
       o->schedule == FD_SCHEDULE_BALANCED ||
       (o->schedule == FD_SCHEDULE_AUTO && o->num_host_seq_lens > 0 && o->force_splits <= 0 &&
-       o->force_chunk_tokens <= 0 && o->heuristic == FD_HEURISTIC_MI355X && ragged &&
-       (int64_t)prob->batch * prob->num_kv_heads <= (int64_t)o->num_cus * o->wgs_per_cu);
+       o->force_chunk_tokens <= 0 && o->heuristic == FD_HEURISTIC_MI355X && ragged && long_enough);
   if (balanced) {
     {
       // The line of granules (see fd_schedule): N workgroups, range w =
       // [floor(w T / N), floor((w + 1) T / N)); S = the most ranges that any
       // one segment meets.
-      // Two resident ranges per CU overlap one range's start-up and drain with
-      // the other's streaming (measured: 219 vs 229-241 us on the paged batch).
+      // One range per CU by default (the caller's wgs_per_cu otherwise): on
+      // ragged batches it was as fast or faster than two (64-sequence edge
+      // batch 54 vs 59 us, 48 sequences of up to 4096 tokens 75 vs 79 us).
       slots = (int64_t)o->num_cus * (balanced_wgs_per_cu > 0 ? balanced_wgs_per_cu : o->wgs_per_cu);
       const int64_t G = tile > paged_align ? tile : paged_align;
       const int64_t H = prob->num_kv_heads;
-      // Default start-up cost of a piece: 256 tokens (sweep on ragged batches:
-      // none 92 us, 128 tokens 62 us, 256 tokens 55 us, 512 tokens 57 us on the
-      // 64-sequence edge batch).
-      const int64_t cost_tok = o->piece_cost_tokens > 0 ? o->piece_cost_tokens : (o->piece_cost_tokens < 0 ? 0 : 256);
+      // Default start-up cost of a piece: 512 tokens (sweep with one range per
+      // CU on sixteen ragged batches: the best of 256, 512 and 1024 tokens, or
+      // within 1 % of it, on every batch where AUTO takes this schedule; no
+      // cost at all was up to 60 % slower).
+      const int64_t cost_tok =
+          o->piece_cost_tokens > 0 ? o->piece_cost_tokens : (o->piece_cost_tokens < 0 ? 0 : FD_DEFAULT_PIECE_COST_TOKENS);
       piece_cost = cdiv64(cost_tok, G);
       auto seg_len = [&](int64_t plen) { return plen > 0 ? plen + piece_cost : 0; };
       int64_t T = 0;

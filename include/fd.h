@@ -103,9 +103,9 @@ typedef enum {
 
 /* How split work is laid out over workgroups. */
 typedef enum {
-  /* BALANCED when the planner has host_seq_lens, the lengths differ, there
-   * are no more (sequence, KV head) segments than workgroup slots, no split
-   * count or chunk is forced and the MI355X rule is in use; else UNIFORM. */
+  /* BALANCED when the planner has host_seq_lens, the lengths differ, their
+   * mean is at least FD_BALANCED_MIN_MEAN_TOKENS, no split count or chunk is
+   * forced and the MI355X rule is in use; else UNIFORM. */
   FD_SCHEDULE_AUTO = 0,
   /* One workgroup per (split, KV head, sequence); split s of every segment is
    * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1). */
@@ -115,13 +115,18 @@ typedef enum {
    * laid end to end, each followed by a few granules that stand for the
    * start-up cost of a piece (q load, first tile, epilogue; no tokens), and
    * cut into N near-equal ranges, one per workgroup
-   * (N = min(CUs x resident workgroups per CU (at most 2), or CUs x
-   * wgs_per_cu when the caller sets it, and cdiv(total granules, 4))). A segment crossing a range
+   * (N = min(CUs, or CUs x wgs_per_cu (at most the resident 2) when the
+   * caller sets it, and cdiv(total granules, 4))). A segment crossing a range
    * boundary yields one state per range: a Stream-K-style partition of the
    * kind kanthi.in §7 lists (LeanAttention) against wave quantization, here
    * so that every workgroup streams the same number of bytes. */
   FD_SCHEDULE_BALANCED = 2
 } fd_schedule;
+
+/* AUTO's threshold for the balanced schedule: the mean host length. */
+#define FD_BALANCED_MIN_MEAN_TOKENS 768
+/* Default start-up cost of one balanced piece, in KV tokens. */
+#define FD_DEFAULT_PIECE_COST_TOKENS 512
 
 /* Shape and layout of one decode step. All strides are in ELEMENTS. */
 typedef struct {
@@ -178,7 +183,8 @@ typedef struct {
   int32_t num_host_seq_lens;  /* entries in host_seq_lens (0: none; else must equal batch) */
   int32_t schedule;           /* fd_schedule */
   int32_t piece_cost_tokens;  /* balanced schedule: start-up cost of one piece, in KV tokens, added
-                                 to every non-empty segment when the line is cut (0: 256; -1: none) */
+                                 to every non-empty segment when the line is cut
+                                 (0: FD_DEFAULT_PIECE_COST_TOKENS; -1: none) */
   int32_t reserved[4];
   /* Optional HOST copy of seq_lens (int32 [batch]). With it the MI355X rule
    * sizes splits from the batch's total work: no split longer than one

@@ -179,8 +179,8 @@ def test_balanced_schedule_matches_oracle(paged):
         plan = fd.fd_plan(prob, num_cus=cus, host_seq_lens=lens, schedule="balanced")
         assert plan.schedule == fd.SCHEDULES["balanced"]
         G = max(32, page)
-        assert plan.slots == cus * 2                   # two resident D=128 16-bit workgroups per CU
-        assert plan.piece_cost == -(-256 // G)           # default start-up cost: 256 tokens
+        assert plan.slots == cus                       # one range per CU by default
+        assert plan.piece_cost == -(-512 // G)           # default start-up cost: 512 tokens
         N, S, _, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots, cost=plan.piece_cost)
         assert (plan.grid_x, plan.grid_y, plan.grid_z) == (N, 1, 1), (lens, cus)
         assert plan.num_splits == S and plan.chunk_tokens == G
@@ -195,18 +195,24 @@ def test_schedule_selection():
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, schedule="uniform").schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, force_splits=4).schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, heuristic="fa2").schedule == fd.SCHEDULES["uniform"]
-    # equal lengths, or more segments than slots: uniform
+    # equal lengths, or short ones on average: uniform
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=[3000] * 3).schedule == fd.SCHEDULES["uniform"]
-    many = contiguous_problem(B=40, Hq=32, Hkv=8, L=3000)                   # 320 segments > 256 slots
+    many = contiguous_problem(B=40, Hq=32, Hkv=8, L=3000)                   # 320 segments, more than the slots
     many_lens = [3000 - (i % 7) for i in range(40)]
-    assert fd.fd_plan(many, num_cus=256, host_seq_lens=many_lens).schedule == fd.SCHEDULES["uniform"]
-    assert fd.fd_plan(many, num_cus=256, host_seq_lens=many_lens,
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=many_lens).schedule == fd.SCHEDULES["balanced"]
+    short = [767 + (i % 2) * 2 for i in range(40)]                           # mean 768
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=short).schedule == fd.SCHEDULES["balanced"]
+    short = [766 + (i % 2) * 2 for i in range(40)]                           # mean 767
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=short).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(many, num_cus=256, host_seq_lens=short,
                       schedule="balanced").schedule == fd.SCHEDULES["balanced"]
     # the VALU kernel (MHA) has its balanced variant too
     mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=3000)
     p = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens)
     assert p.kernel == fd.KERNELS["valu"] and p.schedule == fd.SCHEDULES["balanced"]
-    assert p.slots == 512                               # two resident balanced workgroups per CU at most
+    assert p.slots == 256                               # one range per CU by default
+    p2 = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, wgs_per_cu=4)
+    assert p2.slots == 512                              # two resident balanced workgroups per CU at most
     with pytest.raises(fd.FdError):
         fd.fd_plan(prob, num_cus=256, schedule="balanced")            # needs host lengths
     with pytest.raises(fd.FdError):
