@@ -302,6 +302,35 @@ def test_fused_matches_oracle(case):
     H.check_against_oracle(w, out, lse)
 
 
+# The fused tail folds each row in batches of splits per lane (16 in the MFMA
+# kernel, 8 in the VALU one) over one to four waves per row: split counts
+# beyond one batch, every waves-per-row choice and both workspace forms.
+FUSED_TAIL_CASES = [
+    # (kernel, g, q_len, D, dtype, splits, ws_format)
+    ("mfma", 8, 1, 128, "f16", 33, "uml"),      # 8 rows, two batches per lane group
+    ("mfma", 8, 2, 128, "bf16", 65, "olse"),    # 16 rows (two column tiles), three batches
+    ("mfma", 2, 1, 128, "f16", 70, "uml"),      # 2 rows: two waves per row
+    ("mfma", 3, 1, 64, "bf16", 70, "olse"),     # 3 rows, D=64 (four lane groups per wave)
+    ("mfma", 1, 2, 64, "f16", 129, "uml"),      # 2 rows of a query block, 129 splits
+    ("valu", 1, 1, 128, "bf16", 70, "olse"),    # 1 row: four waves per row, batches of 8
+    ("valu", 2, 1, 128, "f32", 37, "uml"),
+    ("valu", 3, 1, 64, "f16", 50, "uml"),
+]
+
+
+@pytest.mark.parametrize("kernel,g,q_len,D,dtype,splits,ws_format", FUSED_TAIL_CASES)
+def test_fused_tail_batches(kernel, g, q_len, D, dtype, splits, ws_format):
+    lens = [splits * 64, 1, 0, splits * 40 + 3]        # full, one token, empty, trailing splits empty
+    w = W.contiguous(f"fused_tail_{kernel}_g{g}_q{q_len}_S{splits}", seed=90 + splits, batch=len(lens),
+                     q_heads=2 * g, kv_heads=2, head_dim=D, capacity=max(lens), seq_lens=lens, dtype=dtype,
+                     q_len=q_len)
+    plan, out, lse, ctr = _run_fused(w, kernel=kernel, force_splits=splits, ws_format=ws_format,
+                                     host_seq_lens=None)
+    assert plan.num_splits == splits and plan.kernel == fd.KERNELS[kernel]
+    assert torch.all(ctr == 0).item(), "counters must be back at zero"
+    H.check_against_oracle(w, out, lse)
+
+
 def test_fused_repeated_calls_reset_counters():
     w1 = W.contiguous("fused_rep1", seed=84, batch=2, q_heads=16, kv_heads=2, head_dim=128, capacity=4000,
                       seq_lens=[4000, 2500], dtype="f16")
