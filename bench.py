@@ -309,6 +309,21 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # every byte a step moves, beside the K/V bytes the metric counts
+    if w0.paged:
+        page = w0.k.shape[1]
+        bt_bytes = sum(-(-int(n) // page) for n in w0.seq_lens.tolist()) * 4
+    else:
+        bt_bytes = 0
+    moved = {
+        "kv": step_kv,
+        "q": w0.q.numel() * w0.q.element_size(),
+        "out_lse": (out.numel() + lse.numel()) * 4,
+        "workspace_rw": 2 * (plan.ws_o_bytes + plan.ws_stats_bytes),   # written by the split, read by the merge
+        "block_table": bt_bytes,
+        "seq_lens": w0.seq_lens.numel() * 4,
+    }
+    moved["total"] = sum(moved.values())
     tbps = step_kv / (us_step * 1e-6) / 1e12
     achieved = step_kv / (split_us * 1e-6) / 1e9
     khash = kernel_source_hash()
@@ -341,6 +356,7 @@ def main():
         "split_kernel_us": round(split_us, 2),
         "merge_kernel_us": round(merge_us, 2),
         "merge_share": round(merge_us / max(split_us + merge_us, 1e-9), 4),
+        "bytes_per_step": moved,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
