@@ -3,18 +3,18 @@
 // ("Flash-Decoding: Split-KV Attention for Long-Context Decode", kanthi.in,
 // §2 stable form; xuujii KB "Decode 专项 Attention" §04).
 //
-// Two forms. The merge kernel gives each row SG groups of D/4 lanes and folds
-// split by split (its many workgroups keep the memory system busy). The fused
-// tail, where one workgroup merges a whole group of rows, needs more loads in
-// flight per lane: there one wave (or WPR waves) merges one row. Lane (grp, dl) covers dims
-// [4 dl, 4 dl + 4) (D/4 lanes per group) of splits grp, grp + NG, ... where NG
-// is the number of lane groups on the row. A lane issues the loads of
-// NB of its splits together and folds the batch into its running
-// state with one rescale to the larger maximum, so a row of S splits costs
-// about S / (NG * NB) memory round trips. The lane groups are then
-// combined by cross-lane shuffles and, with WPR > 1, through LDS. A split
-// whose m (lse) is -inf weighs exactly 0; a row whose splits are all empty
-// gives O = 0 and LSE = -inf. Every sum has a fixed order.
+// Two forms.
+// - Merge kernel: each row gets SG groups of D/4 lanes that fold its splits
+//   split by split; its many workgroups keep the memory system busy.
+// - Fused tail: one workgroup merges a whole group of rows, so it needs more
+//   loads in flight per lane. One wave (or WPR waves) takes a row; lane
+//   (grp, dl) covers dims [4 dl, 4 dl + 4) of splits grp, grp + NG, ... (NG
+//   lane groups on the row), issues the loads of NB of them together and
+//   folds the batch with one rescale to the larger maximum, so a row of S
+//   splits costs about S / (NG * NB) memory round trips. The lane groups are
+//   combined by cross-lane shuffles and, with WPR > 1, through LDS.
+// A split whose m (lse) is -inf weighs exactly 0; a row whose splits are all
+// empty gives O = 0 and LSE = -inf. Every sum has a fixed order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -96,11 +96,9 @@ __host__ __device__ inline int split_groups_log2(int S, int lanes_per_row, int r
 
 // ---- fused tail (states published in the same launch): one or more waves per row.
 
-
-// Cache policy bits of the state loads. COHERENT (sc1) is the form the
-// compiler gives agent-scope atomic loads on gfx950: it reads states that
+// Cache policy bits of the fused tail's state loads: sc1, the form the
+// compiler gives agent-scope atomic loads on gfx950, so they read states that
 // other workgroups of the same launch published with device-coherent stores.
-constexpr int LOAD_PLAIN = 0;
 constexpr int LOAD_COHERENT = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* base, uint32_t bytes) {
@@ -118,7 +116,7 @@ __device__ __forceinline__ const float* uniform_ptr(const float* p) {
 // Fold splits gi, gi + NG, ... of one row into a lane state. ws_row and st_row
 // (wave-uniform) are the row's first split vector and statistic.
 // NB: splits whose loads one lane has in flight together.
-template <int D, bool UML, int POLICY, int NB>
+template <int D, bool UML, int NB>
 __device__ __forceinline__ RowState fold_row(const float* ws_row, const float* st_row, int S, int gi, int NG, int dl) {
   constexpr int SW = UML ? 2 : 1;
   const __amdgpu_buffer_rsrc_t ru = row_rsrc(ws_row, (uint32_t)S * D * 4);
@@ -135,14 +133,14 @@ __device__ __forceinline__ RowState fold_row(const float* ws_row, const float* s
       l[j] = 0.f;
       if (s < S) {                              // issued back to back; first used after the batch
         u[j] = __builtin_bit_cast(mf32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, (uint32_t)(s * D + 4 * dl) * 4,
-                                                                              0, POLICY));
+                                                                              0, LOAD_COHERENT));
         if (UML) {
           const mf32x2 ml =
-              __builtin_bit_cast(mf32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)s * 8, 0, POLICY));
+              __builtin_bit_cast(mf32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)s * 8, 0, LOAD_COHERENT));
           m[j] = ml.x;
           l[j] = ml.y;
         } else {
-          m[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)s * 4, 0, POLICY));
+          m[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)s * 4, 0, LOAD_COHERENT));
           l[j] = 1.f;
         }
       }
@@ -218,7 +216,7 @@ __host__ __device__ inline int waves_per_row_log2(int rows, int nw) {
 // One pass of the workgroup over NW >> wpr_log2 rows: waves [k WPR, k WPR + WPR)
 // merge state row `row` (wave-uniform; `active` false for a wave without a row).
 // Every thread of the workgroup calls it; with wpr_log2 > 0 it holds barriers.
-template <int D, int NW, int POLICY, int NB>
+template <int D, int NW, int NB>
 __device__ __forceinline__ void merge_row_pass(int64_t row, bool active, int S, bool uml, int wpr_log2,
                                                const float* ws_o, const float* ws_stats, float* out, float* lse,
                                                MergeLds<NW>& sh) {
@@ -235,7 +233,7 @@ __device__ __forceinline__ void merge_row_pass(int64_t row, bool active, int S, 
     const float* sr = uniform_ptr(ws_stats + row * S * (uml ? 2 : 1));
     const int NG = SGW << wpr_log2;
     const int gi = wsub * SGW + grp;
-    st = uml ? fold_row<D, true, POLICY, NB>(wr, sr, S, gi, NG, dl) : fold_row<D, false, POLICY, NB>(wr, sr, S, gi, NG, dl);
+    st = uml ? fold_row<D, true, NB>(wr, sr, S, gi, NG, dl) : fold_row<D, false, NB>(wr, sr, S, gi, NG, dl);
     st = wave_combine<LPR>(st);
   }
   if (wpr_log2 == 0) {
@@ -315,7 +313,7 @@ __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, i
   for (int r0 = 0; r0 < p.R; r0 += per_pass) {            // the group's rows, per_pass of them at a time
     const bool active = r0 + k < p.R;
     const int64_t row = state_row(p, b, kvh, active ? r0 + k : 0);
-    merge_row_pass<D, NWV, LOAD_COHERENT, NB>(row, active, p.S, uml, wpr_log2, p.ws_o, p.ws_stats, p.out, p.lse, sh);
+    merge_row_pass<D, NWV, NB>(row, active, p.S, uml, wpr_log2, p.ws_o, p.ws_stats, p.out, p.lse, sh);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(p.counters + (int64_t)b * p.Hkv + kvh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
