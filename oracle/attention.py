@@ -16,7 +16,7 @@ Sources (pages are cited by title and section):
 * [AIFETCHLY] "FlashDecoding: Fast Long-Context Generation Guide": the fixed
   chunk C (1024) partition.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * A query row whose sequence has no visible key (seq_len = 0) returns
   o = 0 and LSE = −∞, the same convention as an empty split ([KANTHI] §4;
