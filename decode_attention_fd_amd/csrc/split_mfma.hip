@@ -324,12 +324,17 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
     // One exit at the bottom: the wait-count analysis then sees the same load
     // order on entry and on the back edge.
     const int my_tiles = (ntiles - wave + NW - 1) / NW;     // > 0 only if wave < ntiles
-    for (int it = 0; it < my_tiles; ++it, tile += NW) {
+    for (int it = 0; it + 1 < my_tiles; ++it, tile += NW) {
       store(kr, ldsK);
       issue(kr, kbase, tstart(tile + NW), pid_next);
       store(vr, ldsV);
       issue(vr, vbase, tstart(tile + NW), pid_next);
       if (PAGED) pid_next = page_ids(tstart(tile + 2 * NW));
+      compute(start + tile * TT);
+    }
+    if (my_tiles > 0) {                                     // the wave's last tile: nothing more to request
+      store(kr, ldsK);
+      store(vr, ldsV);
       compute(start + tile * TT);
     }
   }
