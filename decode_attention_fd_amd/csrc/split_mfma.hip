@@ -83,6 +83,8 @@ template <int D> struct Geo {
   static constexpr int NDC = D / 32;        // QK^T k-blocks of 32 dims
   static constexpr int NDB = D / 16;        // PV output blocks (dims d = NDB*m + e)
   static constexpr int VW = NDB / 2;        // dwords of V one lane reads per token (4 or 2)
+  static constexpr int OWP = D + 4;         // floats per column of a wave state in LDS: the 16
+                                            // columns of one store fall on different banks
 };
 
 template <int N> struct VRead;
@@ -346,13 +348,13 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
     float l = l_run[ct];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    float* ow = reinterpret_cast<float*>(lds[wave][ct]);   // [16 columns][D] fp32 (<= TILEB bytes)
+    float* ow = reinterpret_cast<float*>(lds[wave][ct]);   // [16 columns][OWP] fp32 (<= TILEB bytes)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e4 = 0; e4 < G::NDB; e4 += 4) {
         f32x4 v = {oacc[ct][e4][i], oacc[ct][e4 + 1][i], oacc[ct][e4 + 2][i], oacc[ct][e4 + 3][i]};
-        *reinterpret_cast<f32x4*>(ow + col * D + G::NDB * (4 * grp + i) + e4) = v;
+        *reinterpret_cast<f32x4*>(ow + col * G::OWP + G::NDB * (4 * grp + i) + e4) = v;
       }
     if (grp == 0) {
       st_m[wave][16 * ct + col] = m_run[ct];
@@ -379,7 +381,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
         const float mw = st_m[w2][16 * ct + c];
         const float a = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
         const float* o = reinterpret_cast<const float*>(lds[w2][ct]);
-        U += a * (o[c * D + d] + o[(c + rt) * D + d]);
+        U += a * (o[c * G::OWP + d] + o[(c + rt) * G::OWP + d]);
         L += a * st_l[w2][16 * ct + c];
       }
     }
