@@ -364,44 +364,66 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
   __syncthreads();
 
   // ---- merge the four wave states (exact rescale to the common max) and
-  // combine the high/low columns, then write the split's state.
-  for (int idx = threadIdx.x; idx < R * D; idx += NW * 64) {
-    const int h = idx / D;                     // state row
-    const int d = idx - h * D;
+  // combine the high/low columns, then write the split's state; a thread
+  // takes four consecutive dims of a row.
+  constexpr int D4 = D / 4;
+  for (int idx = threadIdx.x; idx < R * D4; idx += NW * 64) {
+    const int h = idx / D4;                    // state row
+    const int d = (idx - h * D4) * 4;
     const int ct = NCT == 1 ? 0 : h >> 3;      // its column tile
     const int c = NCT == 1 ? h : h & 7;        // and column
     const int rt = NCT == 1 ? R : min(8, R - 8 * ct);
     float M = -INFINITY;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, st_m[w2][16 * ct + c]);
-    float U = 0.f, L = 0.f;
+    f32x4 U = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) {
         const float mw = st_m[w2][16 * ct + c];
         const float a = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
         const float* o = reinterpret_cast<const float*>(lds[w2][ct]);
-        U += a * (o[c * G::OWP + d] + o[(c + rt) * G::OWP + d]);
+        U += a * (*reinterpret_cast<const f32x4*>(o + c * G::OWP + d) +
+                  *reinterpret_cast<const f32x4*>(o + (c + rt) * G::OWP + d));
         L += a * st_l[w2][16 * ct + c];
       }
     }
     const int64_t row = state_row(p, b, kvh, h);
     const int64_t base = row * p.S + slot;
     const bool co = p.fused != 0;
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
     if (direct) {                              // one piece: the state is the row's result
-      const bool empty = !(L > 0.f);
-      p.out[row * D + d] = empty ? 0.f : U / L;
+      *reinterpret_cast<f32x4*>(p.out + row * D + d) = U * inv;
       if (d == 0 && p.lse) p.lse[row] = empty ? -INFINITY : (M + log2f(L)) * LN2;
-    } else if (p.ws_format == FD_WS_UML) {
-      ws_store(p.ws_o + base * D + d, U, co);
-      if (d == 0) {
-        ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
-        ws_store(p.ws_stats + base * 2 + 1, L, co);
-      }
     } else {
-      const bool empty = !(L > 0.f);
-      ws_store(p.ws_o + base * D + d, empty ? 0.f : U / L, co);
-      if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
+      const bool uml = p.ws_format == FD_WS_UML;
+      const f32x4 v = uml ? U : U * inv;
+      float* dst = p.ws_o + base * D + d;
+      if (!co) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else if (p.q_len == 1) {
+        // One 16-byte device-coherent store (sc1, as ws_store's agent-scope
+        // atomic stores) into the group's contiguous block of state rows.
+        const float* blk = p.ws_o + state_row(p, b, kvh, 0) * p.S * D;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(blk), (short)0, (int)((int64_t)R * p.S * D * 4),
+                                              0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v),
+                                               rs, (int)(((int64_t)h * p.S + slot) * D + d) * 4, 0, 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ws_store(dst + e, v[e], true);
+      }
+      if (d == 0) {
+        if (uml) {
+          ws_store(p.ws_stats + base * 2, M == -INFINITY ? -INFINITY : M * LN2, co);
+          ws_store(p.ws_stats + base * 2 + 1, L, co);
+        } else {
+          ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
+        }
+      }
     }
   }
 }
