@@ -127,9 +127,13 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   const int r0 = threadIdx.x * E;
   const int r1 = min(B, r0 + E);
   int64_t local = 0;
+  int n1 = 0;                          // the row's length when each thread has one row
   for (int r = r0; r < r1; ++r) {
     const int n = clamp_len(p, r);
-    if (E == 1) sh.len[threadIdx.x] = n;
+    if (E == 1) {
+      sh.len[threadIdx.x] = n;
+      n1 = n;
+    }
     const int64_t pl = (n + G - 1) / G;
     local += H * (pl > 0 ? pl + C : 0);
   }
@@ -160,7 +164,7 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   int cand = B;
   int64_t cand_x = 0;
   for (int r = r0; r < r1; ++r) {
-    const int64_t pl = (clamp_len(p, r) + G - 1) / G;
+    const int64_t pl = ((E == 1 ? n1 : clamp_len(p, r)) + G - 1) / G;   // no second read of seq_lens
     const int64_t xn = x + H * (pl > 0 ? pl + C : 0);
     if (x >= gs || xn > gs) {
       cand = r;
