@@ -55,7 +55,8 @@ def make_workload(name: str, device):
     return builders[name]()
 
 
-def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0, kernel: str = "auto") -> dict:
+def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0, kernel: str = "auto",
+                 piece_cost: int = 0) -> dict:
     """fd_plan options of a benchmark run: the workload's forced splits or
     chunk if it has them, else the planner fed the host copy of the lengths."""
     opts = {"ws_format": w.ws_format}
@@ -72,6 +73,8 @@ def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0
         opts["wgs_per_cu"] = wgs_per_cu
     if kernel != "auto":
         opts["kernel"] = kernel
+    if piece_cost:
+        opts["piece_cost_tokens"] = piece_cost
     return opts
 
 
@@ -198,6 +201,8 @@ def main():
                     help="split schedule (auto: balanced when the planner gets the host lengths and can use it)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner slots per CU (0 = library default)")
     ap.add_argument("--kernel", choices=["auto", "mfma", "valu"], default="auto", help="split kernel (auto: planner)")
+    ap.add_argument("--piece-cost", type=int, default=0,
+                    help="balanced schedule: start-up cost of one piece in KV tokens (0 = library default, -1 = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
@@ -231,7 +236,7 @@ def main():
     ws = [w0] + [W.redraw_kv(w0, 7000 + i) for i in range(1, copies)]
     torch.cuda.synchronize()
 
-    opts = plan_options(w0, args.splits, args.schedule, args.wgs_per_cu, args.kernel)
+    opts = plan_options(w0, args.splits, args.schedule, args.wgs_per_cu, args.kernel, args.piece_cost)
     prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
     t0 = time.perf_counter()
     plan = fd.fd_plan(prob, **opts)
