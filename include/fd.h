@@ -84,8 +84,8 @@ typedef enum {
 } fd_ws_format;
 
 typedef enum {
-  FD_KERNEL_AUTO = 0,  /* MFMA for 16-bit KV with 2 <= g <= 8, VALU otherwise */
-  FD_KERNEL_MFMA = 1,  /* packed-GQA tile on MFMA 16x16x32 (16-bit KV, g <= 8) */
+  FD_KERNEL_AUTO = 0,  /* MFMA for 16-bit KV with 2 <= g * q_len <= 16, VALU otherwise */
+  FD_KERNEL_MFMA = 1,  /* packed-GQA tile on MFMA 16x16x32 (16-bit KV, g * q_len <= 16) */
   FD_KERNEL_VALU = 2   /* one query head per lane row, DPP dot products */
 } fd_kernel;
 
