@@ -318,20 +318,25 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
   if (ntiles > 0) {
     u32x4 kr[G::NI], vr[G::NI];
     int tile = wave;
-    int pid = 0, pid_next = 0;
+    // Paged: the block-table entries of a tile are requested before the K/V
+    // loads of the tile before it. Loads complete in order, so they have
+    // arrived once that K tile has, and requesting the next K tile never waits
+    // for the V tile still in flight.
+    int pid = 0, pid_next = 0, pid_after = 0;
     if (PAGED) pid = page_ids(tstart(tile));
+    if (PAGED) pid_next = page_ids(tstart(tile + NW));
     issue(kr, kbase, tstart(tile), pid);
     issue(vr, vbase, tstart(tile), pid);
-    if (PAGED) pid_next = page_ids(tstart(tile + NW));
     // One exit at the bottom: the wait-count analysis then sees the same load
     // order on entry and on the back edge.
     const int my_tiles = (ntiles - wave + NW - 1) / NW;     // > 0 only if wave < ntiles
     for (int it = 0; it + 1 < my_tiles; ++it, tile += NW) {
+      if (PAGED) pid_after = page_ids(tstart(tile + 2 * NW));
       store(kr, ldsK);
       issue(kr, kbase, tstart(tile + NW), pid_next);
       store(vr, ldsV);
       issue(vr, vbase, tstart(tile + NW), pid_next);
-      if (PAGED) pid_next = page_ids(tstart(tile + 2 * NW));
+      if (PAGED) pid_next = pid_after;
       compute(start + tile * TT);
     }
     if (my_tiles > 0) {                                     // the wave's last tile: nothing more to request

@@ -207,14 +207,19 @@ __device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>&
   }
   const float c2 = p.scale_log2;
 
+  // Loads are unconditional (addresses of rows past the piece are clamped to
+  // its last row) and the wave's last tile is peeled off the loop, so the
+  // wait-count analysis knows exactly which loads are in flight and never has
+  // to drain them all inside the loop.
+  const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
   int tile = wave;
   int pid_cur = 0, pid_next = 0;
-  if (PAGED) {
-    if (tile < ntiles) pid_cur = page_ids(start + tile * TT);
-    if (tile + NW < ntiles) pid_next = page_ids(start + (tile + NW) * TT);
-  }
-  if (tile < ntiles) {
+  if (my_tiles > 0) {
     const int t0 = start + tile * TT;
+    if (PAGED) {
+      pid_cur = page_ids(t0);
+      pid_next = page_ids(t0 + NW * TT);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t off = offset(t0, u, pid_cur);
@@ -223,17 +228,23 @@ __device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>&
     }
   }
 
-  for (; tile < ntiles; tile += NW) {
+  // One tile; with `more` the wave's next tile (tile + NW) exists and is
+  // requested: K after the scores, V after the PV update.
+  auto step = [&](int tile, bool more) {
     const int t0 = start + tile * TT;
-    const int nt = tile + NW;
-    const int tn0 = start + nt * TT;
+    const int tn0 = t0 + NW * TT;
+    // Paged: the block-table entries of the tile after next are requested
+    // before the next tile's K/V loads; loads complete in order, so they have
+    // arrived once that K tile has, and requesting K never waits for a V tile.
+    int pid_after = 0;
+    if (PAGED && more) pid_after = page_ids(tn0 + NW * TT);
 
     float x[G][U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int h = 0; h < G; ++h) x[h][u] = Elt<T>::dot(q[h], kb[u]);
-    if (nt < ntiles) {
+    if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + offset(tn0, u, pid_next)));
     }
@@ -287,12 +298,14 @@ __device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>&
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[h][e] = fmaf(x[h][u], v, acc[h][e]);
       }
-    if (nt < ntiles) {
+    if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) vb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + offset(tn0, u, pid_next)));
-      if (PAGED && nt + NW < ntiles) pid_next = page_ids(start + (nt + NW) * TT);
+      if (PAGED) pid_next = pid_after;
     }
-  }
+  };
+  for (int it = 0; it + 1 < my_tiles; ++it, tile += NW) step(tile, true);
+  if (my_tiles > 0) step(tile, false);
 
   // ---- row-group states -> LDS, then one exact merge per (head, dim)
 #pragma unroll
