@@ -89,11 +89,11 @@ def choose_path(plan, path: str = "auto") -> str:
     return "fused" if plan.num_splits == 1 or plan.schedule == fd.SCHEDULES["balanced"] else "split"
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the MFMA split kernel is compiled from (the kernel
-    the roofline and the traffic record describe)."""
+def kernel_source_hash(kernel: str = "mfma") -> str:
+    """Hash of the sources a split kernel ("mfma" or "valu") is compiled from
+    (the kernel the roofline and the traffic record describe)."""
     h = hashlib.sha256()
-    for rel in ("decode_attention_fd_amd/csrc/split_mfma.hip", "decode_attention_fd_amd/csrc/balance.h",
+    for rel in (f"decode_attention_fd_amd/csrc/split_{kernel}.hip", "decode_attention_fd_amd/csrc/balance.h",
                 "decode_attention_fd_amd/csrc/merge_rows.h", "decode_attention_fd_amd/csrc/fd_internal.h",
                 "include/fd.h"):
         with open(os.path.join(ROOT, rel), "rb") as fh:
@@ -134,7 +134,10 @@ def _pmc_rows(d: str, counter: str):
 def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> None:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, scaled by the
     same counters on the calibration copy (COPY_BYTES read and written)."""
-    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    names = [n for n, _ in _pmc_rows(fetch_dir, "FETCH_SIZE") if "split_" in n and "kernel" in n]
+    kernel = "valu" if names and all("split_valu" in n for n in names) else "mfma"
+    out = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
+           "copy_bytes": COPY_BYTES}
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _pmc_rows(d, counter)
         split = [v for n, v in rows if "split_" in n and "kernel" in n]
@@ -331,7 +334,7 @@ def main():
     moved["total"] = sum(moved.values())
     tbps = step_kv / (us_step * 1e-6) / 1e12
     achieved = step_kv / (split_us * 1e-6) / 1e9
-    khash = kernel_source_hash()
+    khash = kernel_source_hash({1: "mfma", 2: "valu"}[plan.kernel])
     traffic = traffic_from_profile(args.workload, khash)
     result = {
         "metric": "decode-attention µs/layer-step and achieved HBM TB/s (% of peak), B=1 L=128k GQA",
