@@ -1,0 +1,76 @@
+"""Host logic of bench.py (no GPU): the one-GPU rule, the scaling of the
+rocprofv3 counters by the calibration copy, the source-hash check that keeps
+a stale traffic record out of the JSON line, and the committed records."""
+import glob
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from tests.conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=300)
+    assert r.returncode != 0
+    assert "--gpus 1" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def _counter_csv(d, counter, rows):
+    os.makedirs(d)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f'"{name}",{counter},{value}\n')
+
+
+def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    split = "void fd::(anonymous namespace)::split_valu_kernel<128>(fd::SplitParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    copy_kib = bench.COPY_BYTES / 1024 / 2          # the counter reads half of a known copy
+    _counter_csv(str(tmp_path / "f"), "FETCH_SIZE",
+                 [(split, 1000.0), (split, 1002.0), (copy, 10.0), (copy, copy_kib)])
+    _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", [(split, 8.0), (copy, bench.COPY_BYTES / 1024)])
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel="mfma": f"hash-{kernel}")
+    bench.pmc_summary("wl", str(tmp_path / "f"), str(tmp_path / "w"))
+    rec = json.load(open(tmp_path / "profiles" / "traffic_split_wl.json"))
+    assert rec["kernel"] == "valu" and rec["kernel_source_hash"] == "hash-valu"
+    assert rec["fetch"]["scale"] == pytest.approx(2.0)
+    assert rec["fetch"]["bytes_per_launch"] == pytest.approx(1001.0 * 1024 * 2)
+    assert rec["write"]["bytes_per_launch"] == pytest.approx(8.0 * 1024)
+    assert rec["bytes_per_launch"] == pytest.approx(1001.0 * 2048 + 8.0 * 1024)
+    # the record is used only while the sources it was taken on are unchanged
+    assert bench.traffic_from_profile("wl", "hash-valu") == pytest.approx(rec["bytes_per_launch"])
+    assert bench.traffic_from_profile("wl", "hash-mfma") is None
+    assert bench.traffic_from_profile("other", "hash-valu") is None
+
+
+def test_source_hash_names_its_kernel():
+    assert bench.kernel_source_hash("mfma") != bench.kernel_source_hash("valu")
+    assert bench.kernel_source_hash("mfma") == bench.kernel_source_hash()
+
+
+def test_committed_traffic_records_are_consistent():
+    paths = glob.glob(os.path.join(ROOT, "profiles", "traffic_split_*.json"))
+    assert any(p.endswith("traffic_split_gqa64x8_f16_L128000.json") for p in paths)
+    for p in paths:
+        rec = json.load(open(p))
+        assert os.path.basename(p) == f"traffic_split_{rec['workload']}.json"
+        assert rec["workload"] in bench.WORKLOADS
+        assert rec.get("kernel", "mfma") in ("mfma", "valu")
+        assert len(rec["kernel_source_hash"]) == 16
+        assert rec["bytes_per_launch"] == pytest.approx(rec["fetch"]["bytes_per_launch"] +
+                                                        rec["write"]["bytes_per_launch"])
+        for key in ("fetch", "write"):
+            c = rec[key]
+            assert c["scale"] == pytest.approx(rec["copy_bytes"] / (c["copy_kib_per_dispatch"] * 1024))
+            assert c["bytes_per_launch"] == pytest.approx(c["split_kib_per_dispatch"] * 1024 * c["scale"])
