@@ -132,3 +132,43 @@ def test_bench_launch_configuration(name):
     assert (plan2.num_splits, plan2.chunk_tokens, plan2.schedule) == (plan.num_splits, plan.chunk_tokens, plan.schedule)
     _finite_everywhere(out, lse, w.seq_lens)
     H.check_against_oracle(w, out, lse, H.sample_pairs(w.batch, w.num_q_heads, 16, seed=11))
+
+
+def _sample_pairs(B, Hq, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({(int(rng.integers(0, B)), int(rng.integers(0, Hq))) for _ in range(n)} | {(0, 0), (B - 1, Hq - 1)})
+
+
+@pytest.mark.parametrize("case", ["rows_4096", "splits_1024", "balanced_rows_1000", "balanced_fused_rows_1000"])
+def test_large_grids(case):
+    """Grids far larger than the workloads': 4096 sequences of short ragged
+    lengths (a (1, 2, 4096) uniform grid), one sequence forced into 1024 mostly
+    short or empty splits, and the balanced schedule over 1000 sequences (four
+    rows per thread in its scan, lengths read back from memory in its walk),
+    split + merge and fused; sampled rows against the oracle, every row finite."""
+    rng = np.random.default_rng(3000)
+    if case == "rows_4096":
+        lens = [int(x) for x in rng.integers(0, 80, 4096)]
+        w = W.contiguous(case, seed=3001, batch=4096, q_heads=8, kv_heads=2, head_dim=64, capacity=80,
+                         seq_lens=lens, dtype="f16")
+        plan, out, lse, _, _ = H.run(w)
+    elif case == "splits_1024":
+        w = W.contiguous(case, seed=3002, batch=1, q_heads=16, kv_heads=2, head_dim=128, capacity=40000,
+                         seq_lens=[40000], dtype="bf16")
+        plan, out, lse, _, _ = H.run(w, force_splits=1024)
+        assert plan.num_splits == 1024
+    else:
+        lens = [int(x) for x in rng.integers(0, 600, 1000)]
+        lens[::97] = [0] * len(lens[::97])
+        w = W.contiguous(case, seed=3003, batch=1000, q_heads=8, kv_heads=2, head_dim=128, capacity=600,
+                         seq_lens=lens, dtype="f16")
+        opts = dict(schedule="balanced", host_seq_lens=lens)
+        if case == "balanced_fused_rows_1000":
+            plan, out, lse, ctr = H.run_fused(w, **opts)
+            assert torch.all(ctr == 0).item()
+        else:
+            plan, out, lse, _, _ = H.run(w, **opts)
+        assert plan.schedule == fd.SCHEDULES["balanced"]
+    H.say(f"{case}: S={plan.num_splits} grid=({plan.grid_x}, {plan.grid_y}, {plan.grid_z}) schedule={plan.schedule}")
+    _finite_everywhere(out, lse, w.seq_lens)
+    H.check_against_oracle(w, out, lse, _sample_pairs(w.batch, w.num_q_heads, 24, 3004))
