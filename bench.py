@@ -170,9 +170,18 @@ def cpu_baseline(w, max_heads: int):
     cache = A.Cache(cpu.q, cpu.k, cpu.v, cpu.seq_lens, cpu.block_table)
     pairs = [(b, h) for b in range(cache.B) for h in range(cache.Hq)][:max_heads]
     A.attention_one(cache, *pairs[0])                       # warm the allocator
-    t0 = time.perf_counter()
-    out = [A.attention_one(cache, b, h) for b, h in pairs]
-    dt = time.perf_counter() - t0
+    # passes over the sample until about 10 s of CPU work (at most 8 passes or
+    # 30 s); the median pass is the sample's time
+    passes = []
+    while True:
+        t0 = time.perf_counter()
+        res = [A.attention_one(cache, b, h) for b, h in pairs]
+        passes.append(time.perf_counter() - t0)
+        if len(passes) == 1:
+            out = res
+        if sum(passes) >= 10.0 or len(passes) >= 8 or sum(passes) + passes[-1] > 30.0:
+            break
+    dt = sorted(passes)[len(passes) // 2]
     # KV bytes the sampled heads stand for, out of the step's total
     lens = cpu.seq_lens.to(torch.int64).tolist()
     per_head_bytes = [lens[b] * 2 * cache.D * cpu.k.element_size() for b, _ in pairs]
@@ -183,8 +192,9 @@ def cpu_baseline(w, max_heads: int):
     return {
         "value": kv_bytes / step_s / 1e12, "unit": "TB/s", "us_per_step": step_s * 1e6, "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(pairs)} of {cache.B * cache.Hq} (sequence, query head) outputs of copy 0 in float64 "
-                  f"({dt:.1f} s), scaled by their share of the step's KV bytes ({sampled_fraction:.3f})",
+        "sample": f"{len(pairs)} of {cache.B * cache.Hq} (sequence, query head) outputs of copy 0 in float64, "
+                  f"{len(passes)} passes in {sum(passes):.1f} s (median pass {dt:.2f} s), scaled by their share of "
+                  f"the step's KV bytes ({sampled_fraction:.3f})",
     }, out, pairs
 
 

@@ -74,3 +74,11 @@ def test_committed_traffic_records_are_consistent():
             c = rec[key]
             assert c["scale"] == pytest.approx(rec["copy_bytes"] / (c["copy_kib_per_dispatch"] * 1024))
             assert c["bytes_per_launch"] == pytest.approx(c["split_kib_per_dispatch"] * 1024 * c["scale"])
+
+
+def test_cpu_baseline_leg_on_the_tiny_workload():
+    w = bench.make_workload("tiny_mha_f32_L1000", "cpu")
+    cb, ref, pairs = bench.cpu_baseline(w, 64)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TB/s" and cb["value"] > 0 and cb["cores"] >= 1
+    assert len(pairs) == 4 and len(ref) == 4
+    assert "passes" in cb["sample"] and "(1.000)" in cb["sample"]
