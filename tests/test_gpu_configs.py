@@ -134,11 +134,6 @@ def test_bench_launch_configuration(name):
     H.check_against_oracle(w, out, lse, H.sample_pairs(w.batch, w.num_q_heads, 16, seed=11))
 
 
-def _sample_pairs(B, Hq, n, seed):
-    rng = np.random.default_rng(seed)
-    return sorted({(int(rng.integers(0, B)), int(rng.integers(0, Hq))) for _ in range(n)} | {(0, 0), (B - 1, Hq - 1)})
-
-
 @pytest.mark.parametrize("case", ["rows_4096", "splits_1024", "balanced_rows_1000", "balanced_fused_rows_1000"])
 def test_large_grids(case):
     """Grids far larger than the workloads': 4096 sequences of short ragged
@@ -171,4 +166,17 @@ def test_large_grids(case):
         assert plan.schedule == fd.SCHEDULES["balanced"]
     H.say(f"{case}: S={plan.num_splits} grid=({plan.grid_x}, {plan.grid_y}, {plan.grid_z}) schedule={plan.schedule}")
     _finite_everywhere(out, lse, w.seq_lens)
-    H.check_against_oracle(w, out, lse, _sample_pairs(w.batch, w.num_q_heads, 24, 3004))
+    H.check_against_oracle(w, out, lse, H.sample_pairs(w.batch, w.num_q_heads, 24, seed=3004))
+
+
+@pytest.mark.parametrize("name", ["long_gqa", "mha_chunked"])
+def test_fused_full_size(name):
+    """The fused call on the two uniform multi-split workloads at full size
+    (32 splits of 4000 tokens for 8 GQA groups; 64 splits of 1024 tokens for 32
+    MHA heads): the last workgroup of each group merges all of its states."""
+    w = W.long_gqa_f16() if name == "long_gqa" else W.mha_bf16_chunked()
+    plan, out, lse, ctr = H.run_fused(w)
+    assert plan.num_splits in (32, 64)
+    assert torch.all(ctr == 0).item()
+    _finite_everywhere(out, lse, w.seq_lens)
+    H.check_against_oracle(w, out, lse, H.sample_pairs(w.batch, w.num_q_heads, 8, seed=3005))
