@@ -82,3 +82,26 @@ def test_cpu_baseline_leg_on_the_tiny_workload():
     assert cb["kind"] == "oracle" and cb["unit"] == "TB/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert len(pairs) == 4 and len(ref) == 4
     assert "passes" in cb["sample"] and "(1.000)" in cb["sample"]
+
+
+def _profile_commands():
+    """The bench.py arguments of every command the profile summaries print."""
+    import re
+
+    cmds = []
+    for md in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        text = open(md).read().replace("\\\n", " ")
+        for line in text.splitlines():
+            m = re.search(r"bench\.py((?: --?[\w-]+(?: [\w./<>-]+)*)*)\s*$", line.strip())
+            if m and "bench.py" in line and "`" not in line:
+                cmds.append((os.path.basename(md), m.group(1).split()))
+    return cmds
+
+
+def test_profile_commands_parse_with_this_bench():
+    cmds = _profile_commands()
+    assert len(cmds) >= 12                      # trace, counter passes and summaries of four workloads
+    parser = bench.build_parser()
+    for md, argv in cmds:
+        args = parser.parse_args(argv)
+        assert args.workload in bench.WORKLOADS, (md, argv)
