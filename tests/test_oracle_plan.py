@@ -121,3 +121,33 @@ def test_balanced_schedule_with_piece_cost():
         for w, lo, hi in lst:
             tokens[w] += hi - lo
     assert tokens[0] < tokens[1]
+
+
+def test_balanced_schedule_worked_example():
+    """A partition worked out by hand from the definition. Lengths [96, 40],
+    two KV heads, 32-token granules, no cost granules, four slots, ranges of
+    at least one granule: segments (0,0), (0,1) hold 3 granules each and
+    (1,0), (1,1) hold 2, so the line has T = 10 granules, in (b, h) order at
+    [0,3), [3,6), [6,8), [8,10). N = 4 ranges: [0,2), [2,5), [5,7), [7,10)
+    (floor(w * 10 / 4)). Each segment's pieces are its intersections with the
+    ranges, in tokens; the last granule of sequence 1 holds tokens 32..39 only."""
+    N, S, pieces, T = P.balanced_schedule([96, 40], 2, 32, 4, min_granules=1)
+    assert (N, S, T) == (4, 2, 10)
+    assert pieces == {
+        (0, 0): [(0, 0, 64), (1, 64, 96)],
+        (0, 1): [(1, 0, 64), (2, 64, 96)],
+        (1, 0): [(2, 0, 32), (3, 32, 40)],
+        (1, 1): [(3, 0, 40)],
+    }
+    # with one cost granule per segment the line grows to 14 and the cuts move:
+    # segments at [0,4), [4,8), [8,11), [11,14) (token granules first, then the
+    # cost granule); ranges [0,3), [3,7), [7,10), [10,14) now each hold one
+    # segment's token granules whole, so every segment is one piece (S = 1)
+    N, S, pieces, T = P.balanced_schedule([96, 40], 2, 32, 4, min_granules=1, cost=1)
+    assert (N, S, T) == (4, 1, 14)
+    assert pieces == {
+        (0, 0): [(0, 0, 96)],
+        (0, 1): [(1, 0, 96)],
+        (1, 0): [(2, 0, 40)],
+        (1, 1): [(3, 0, 40)],
+    }
