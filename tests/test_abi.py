@@ -412,3 +412,16 @@ def test_every_entry_point_is_documented_with_its_source():
         if m.group(1) in ("fd_plan", "fd_decode_split", "fd_merge", "fd_decode_fused", "fd_merge_states"):
             assert re.search(r"kanthi\.in|xuujii|tinyvolt", comment), f"{m.group(1)} cites no page"
         prev_end = src.index(";", m.end()) + 1
+
+
+def test_balanced_plan_worked_example():
+    """The planner on a partition worked out by hand: lengths [320, 96], one KV
+    head, four CUs, no cost granules. Segments hold 10 and 3 granules of 32
+    tokens (T = 13); N = min(4 slots, cdiv(13, 4)) = 4 ranges
+    [0,3), [3,6), [6,9), [9,13). Sequence 0's granules [0,10) meet all four
+    ranges (four pieces), sequence 1's [10,13) only the last: S = 4."""
+    prob = contiguous_problem(B=2, Hq=4, Hkv=1, L=320)
+    plan = fd.fd_plan(prob, num_cus=4, host_seq_lens=[320, 96], schedule="balanced", piece_cost_tokens=-1)
+    assert plan.schedule == fd.SCHEDULES["balanced"] and plan.piece_cost == 0
+    assert (plan.grid_x, plan.grid_y, plan.grid_z) == (4, 1, 1)
+    assert plan.num_splits == 4 and plan.chunk_tokens == 32
