@@ -1,5 +1,6 @@
 """Pins of the oracle's split-count rules (kanthi.in §6; vatshank FA3 comment)."""
 import math
+import pytest
 
 from oracle import plan as P
 from tests.conftest import golden
@@ -151,3 +152,19 @@ def test_balanced_schedule_worked_example():
         (1, 0): [(2, 0, 40)],
         (1, 1): [(3, 0, 40)],
     }
+
+
+def test_length_aware_chunk_worked_example():
+    """By hand: lengths [1000, 3000] over 8 KV heads are 32 000 token-heads of
+    work; one slot's share on 256 slots is cdiv(32000, 256) = 125 tokens,
+    rounded up to the 32-token tile: 128, i.e. S = cdiv(3000, 128) = 24 splits.
+    The workspace check (g = 4, D = 128, fp16) puts 2*24*4*130*4 bytes of
+    states against 2*3000*128*2 of K/V per (sequence, KV head): 0.065 > 0.02.
+    The chunk grows by whole tiles until the ratio fits: 416 tokens still
+    gives S = 8 (0.0217), 448 gives S = 7 (0.0190)."""
+    assert P.workspace_ratio(24, 4, 128, 2, 3000) == pytest.approx(2 * 24 * 4 * 130 * 4 / (2 * 3000 * 128 * 2))
+    assert P.workspace_ratio(24, 4, 128, 2, 3000) > 0.02
+    assert P.workspace_ratio(8, 4, 128, 2, 3000) > 0.02 >= P.workspace_ratio(7, 4, 128, 2, 3000)
+    assert P.chunk_from_lengths([1000, 3000], 3000, 8, 256, 32, 128, 4, 128, 2, 0.02) == 448
+    # without the budget the share alone decides
+    assert P.chunk_from_lengths([1000, 3000], 3000, 8, 256, 32, 128, 4, 128, 2, 1.0) == 128
