@@ -282,7 +282,12 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
     } else {
       slots = (int64_t)o->num_cus * o->wgs_per_cu;
       block = (int64_t)tile * waves;
-      align = tile > paged_align ? tile : paged_align;
+      // Contiguous caches take chunk = cdiv(len, S) exactly: rounding it up to
+      // the wave tile made the split kernel 5-10 % slower at 32k-64k tokens
+      // (e.g. 64 000 tokens over 32 splits: 2000-token chunks 44-45 us, 2016
+      // 47-48 us, 2048 58-62 us), though the last tile of a split is then
+      // partial. Paged splits keep page- and tile-aligned boundaries.
+      align = paged ? (tile > paged_align ? tile : paged_align) : 1;
       budget = o->overhead_budget > 0.0f ? (double)o->overhead_budget : 0.02;
       threshold = 1.0;
     }

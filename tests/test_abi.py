@@ -111,7 +111,7 @@ def test_mi355x_heuristic_matches_oracle_rule(kernel, wgs):
                 block = plan.tile_tokens * plan.waves_per_wg
                 s = OP.num_splits_traffic(B * Hkv, cus * wgs, math.ceil(L / block), 128, g, 128, 2, L, budget,
                                           threshold=1.0)
-                chunk = OP.chunk_for(L, s, plan.tile_tokens)
+                chunk = OP.chunk_for(L, s, 1)              # contiguous: cdiv(L, S), no tile rounding
                 assert plan.chunk_tokens == chunk, (B, Hkv, g, L)
                 assert plan.num_splits == math.ceil(L / chunk), (B, Hkv, g, L)
                 assert plan.num_splits <= s
@@ -141,7 +141,7 @@ def test_length_aware_rule_matches_oracle(paged):
         mk = paged_problem if paged else contiguous_problem
         prob = mk(B=B, Hq=Hkv * g, Hkv=Hkv, L=L)
         plan = fd.fd_plan(prob, num_cus=256, kernel=kernel, host_seq_lens=lens.tolist(), schedule="uniform")
-        align = max(plan.tile_tokens, 16 if paged else 1)
+        align = max(plan.tile_tokens, 16) if paged else 1
         chunk = OP.chunk_from_lengths(lens.tolist(), L, Hkv, 256, align, 128, g, 128, 2, 0.02)
         assert plan.chunk_tokens == chunk, (B, Hkv, g, L, lens.tolist()[:4])
         assert plan.num_splits == math.ceil(L / chunk)
