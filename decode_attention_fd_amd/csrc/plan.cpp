@@ -12,8 +12,8 @@
 // in flight each) already pulls that CU's share of HBM bandwidth, so a wave
 // of work is CUs x 1 workgroups, and any idle CU in the last wave costs
 // bandwidth directly, so the threshold is the best efficiency itself. Blocks
-// are one workgroup iteration (4 waves x 32 tokens); chunks are rounded to the
-// 32-token wave tile only. Split counts whose fp32 workspace traffic (written
+// are one workgroup iteration (4 waves x 32 tokens); chunks are cdiv(len, S),
+// aligned to pages and tiles on paged caches only. Split counts whose fp32 workspace traffic (written
 // by the split kernel and read back by the merge) exceeds a budget of the KV
 // bytes are dropped -- the overhead check at the end of §6, generalised to g
 // query heads per KV head.

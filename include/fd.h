@@ -92,9 +92,10 @@ typedef enum {
 typedef enum {
   /* Wave-efficiency rule of kanthi.in §6 re-derived for a bandwidth-bound
    * kernel on MI355X: slots = CUs x wgs_per_cu (1 by default), the smallest
-   * split count reaching the best last-wave efficiency, chunks rounded to the
-   * 32-token wave tile, and only split counts whose workspace traffic stays
-   * within overhead_budget of the KV bytes (§6 overhead check). */
+   * split count reaching the best last-wave efficiency, chunk = cdiv(len, S)
+   * (paged: rounded up to the page and the 32-token wave tile), and only split
+   * counts whose workspace traffic stays within overhead_budget of the KV
+   * bytes (§6 overhead check). */
   FD_HEURISTIC_MI355X = 0,
   /* The §6 rule exactly as printed: slots = 2 x CUs, block = 128 tokens, no
    * traffic bound. Kept to reproduce the page's table. */
