@@ -180,7 +180,7 @@ typedef struct {
   int32_t kernel;             /* fd_kernel */
   int32_t heuristic;          /* fd_heuristic */
   int32_t max_splits;         /* 0: 128 */
-  float overhead_budget;      /* 0: 0.02 (workspace bytes <= 2% of KV bytes) */
+  float overhead_budget;      /* 0: 0.25 (workspace bytes written and read <= 25% of the KV bytes) */
   int32_t num_host_seq_lens;  /* entries in host_seq_lens (0: none; else must equal batch) */
   int32_t schedule;           /* fd_schedule */
   int32_t piece_cost_tokens;  /* balanced schedule: start-up cost of one piece, in KV tokens, added

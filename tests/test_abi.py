@@ -100,7 +100,7 @@ def test_fa2_heuristic_reproduces_page_table():
 @pytest.mark.parametrize("wgs", [1, 2])
 def test_mi355x_heuristic_matches_oracle_rule(kernel, wgs):
     cus = 256
-    budget = 0.02
+    budget = 0.25                                   # the MI355X default
     for B in (1, 2, 4, 16, 64):
         for Hkv, g in ((8, 8), (8, 4), (32, 1), (2, 2)):
             if (kernel == "mfma" and g == 1) or (kernel == "valu" and g > 4):
@@ -142,7 +142,7 @@ def test_length_aware_rule_matches_oracle(paged):
         prob = mk(B=B, Hq=Hkv * g, Hkv=Hkv, L=L)
         plan = fd.fd_plan(prob, num_cus=256, kernel=kernel, host_seq_lens=lens.tolist(), schedule="uniform")
         align = max(plan.tile_tokens, 16) if paged else 1
-        chunk = OP.chunk_from_lengths(lens.tolist(), L, Hkv, 256, align, 128, g, 128, 2, 0.02)
+        chunk = OP.chunk_from_lengths(lens.tolist(), L, Hkv, 256, align, 128, g, 128, 2, 0.25)
         assert plan.chunk_tokens == chunk, (B, Hkv, g, L, lens.tolist()[:4])
         assert plan.num_splits == math.ceil(L / chunk)
 
