@@ -105,8 +105,10 @@ typedef enum {
 /* How split work is laid out over workgroups. */
 typedef enum {
   /* BALANCED when the planner has host_seq_lens, the lengths differ, their
-   * mean is at least FD_BALANCED_MIN_MEAN_TOKENS, no split count or chunk is
-   * forced and the MI355X rule is in use; else UNIFORM. */
+   * mean is at least FD_BALANCED_MIN_MEAN_TOKENS, the batch holds at least
+   * FD_BALANCED_MIN_RANGE_TOKENS tokens of K/V rows (Hkv * sum of lengths) per
+   * balanced range, no split count or chunk is forced and the MI355X rule is
+   * in use; else UNIFORM. */
   FD_SCHEDULE_AUTO = 0,
   /* One workgroup per (split, KV head, sequence); split s of every segment is
    * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1). */
@@ -124,8 +126,10 @@ typedef enum {
   FD_SCHEDULE_BALANCED = 2
 } fd_schedule;
 
-/* AUTO's threshold for the balanced schedule: the mean host length. */
+/* AUTO's thresholds for the balanced schedule: the mean host length, and the
+ * K/V rows (KV heads x tokens) per balanced range. */
 #define FD_BALANCED_MIN_MEAN_TOKENS 768
+#define FD_BALANCED_MIN_RANGE_TOKENS 768
 /* Default start-up cost of one balanced piece, in KV tokens. */
 #define FD_DEFAULT_PIECE_COST_TOKENS 512
 

@@ -188,9 +188,15 @@ def test_balanced_schedule_matches_oracle(paged):
 
 
 def test_schedule_selection():
-    lens = [3000, 10, 0]
-    prob = contiguous_problem(B=3, Hq=32, Hkv=8, L=3000)
+    lens = [30000, 10, 0]                        # 8 * 30010 / 256 = 937 tokens per range
+    prob = contiguous_problem(B=3, Hq=32, Hkv=8, L=30000)
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens).schedule == fd.SCHEDULES["balanced"]
+    # too little work per range (8 heads x 24 576 tokens over 256 ranges = 768; one token less: 767.97)
+    few = contiguous_problem(B=4, Hq=64, Hkv=8, L=8192)
+    assert fd.fd_plan(few, num_cus=256, host_seq_lens=[8192, 8192, 8191, 1]).schedule == fd.SCHEDULES["balanced"]
+    assert fd.fd_plan(few, num_cus=256, host_seq_lens=[8192, 8192, 8191, 0]).schedule == fd.SCHEDULES["uniform"]
+    assert fd.fd_plan(few, num_cus=256, host_seq_lens=[8192, 8192, 8191, 0],
+                      schedule="balanced").schedule == fd.SCHEDULES["balanced"]
     assert fd.fd_plan(prob, num_cus=256).schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, schedule="uniform").schedule == fd.SCHEDULES["uniform"]
     assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, force_splits=4).schedule == fd.SCHEDULES["uniform"]
@@ -207,12 +213,14 @@ def test_schedule_selection():
     assert fd.fd_plan(many, num_cus=256, host_seq_lens=short,
                       schedule="balanced").schedule == fd.SCHEDULES["balanced"]
     # the VALU kernel (MHA) has its balanced variant too
-    mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=3000)
+    mha = contiguous_problem(B=3, Hq=8, Hkv=8, L=30000)
     p = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens)
     assert p.kernel == fd.KERNELS["valu"] and p.schedule == fd.SCHEDULES["balanced"]
     assert p.slots == 256                               # one range per CU by default
-    p2 = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, wgs_per_cu=4)
+    p2 = fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, wgs_per_cu=4, schedule="balanced")
     assert p2.slots == 512                              # two resident balanced workgroups per CU at most
+    # AUTO counts the work per range over those 512 ranges: 469 tokens, too few
+    assert fd.fd_plan(mha, num_cus=256, host_seq_lens=lens, wgs_per_cu=4).schedule == fd.SCHEDULES["uniform"]
     with pytest.raises(fd.FdError):
         fd.fd_plan(prob, num_cus=256, schedule="balanced")            # needs host lengths
     with pytest.raises(fd.FdError):
