@@ -81,6 +81,19 @@ int validate_problem(const fd_problem* p) {
   if (!(isfinite(p->scale))) return FD_ERR_INVALID_ARG;
   const int64_t elt = dtype_size(p->kv_dtype);
   const int64_t D = p->head_dim;
+  // Strides beyond FD_MAX_STRIDE elements address more memory than any device
+  // holds; bounding them first keeps the byte products below from overflowing.
+  // Only the strides this problem uses are looked at.
+  const bool paged = p->layout == FD_LAYOUT_PAGED;
+  const int64_t strides[] = {p->q_stride_b,
+                             p->q_stride_h,
+                             p->q_len > 1 ? p->q_stride_q : 0,
+                             paged ? p->bt_stride_b : p->kv_stride_b,
+                             paged ? p->pool_stride_page : p->kv_stride_h,
+                             paged ? p->pool_stride_t : p->kv_stride_t,
+                             paged ? p->pool_stride_h : 0};
+  for (int64_t v : strides)
+    if (v > FD_MAX_STRIDE) return FD_ERR_INVALID_ARG;
   if (p->q_stride_h < D || p->q_stride_b < 0) return FD_ERR_INVALID_ARG;
   if ((p->q_stride_h * elt) % 16 || (p->q_stride_b * elt) % 16) return FD_ERR_ALIGNMENT;
   if (p->q_len < 0 || p->q_len > 8) return FD_ERR_UNSUPPORTED;

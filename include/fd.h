@@ -130,6 +130,12 @@ typedef enum {
  * K/V rows (KV heads x tokens) per balanced range. */
 #define FD_BALANCED_MIN_MEAN_TOKENS 768
 #define FD_BALANCED_MIN_RANGE_TOKENS 768
+
+/* Largest accepted stride, in elements, of any fd_problem stride field the
+ * problem uses (2^40: more than any device memory holds). A larger one is
+ * FD_ERR_INVALID_ARG. */
+#define FD_MAX_STRIDE ((int64_t)1 << 40)
+
 /* Default start-up cost of one balanced piece, in KV tokens. */
 #define FD_DEFAULT_PIECE_COST_TOKENS 512
 

@@ -273,6 +273,28 @@ def test_problem_validation():
     assert _status(contiguous_problem(Hq=64, Hkv=8, dtype=0)) == fd.FD_ERR_UNSUPPORTED    # fp32, g = 8
     assert _status(contiguous_problem(Hq=256, Hkv=8)) == fd.FD_ERR_UNSUPPORTED            # g = 32
     assert _status(contiguous_problem(dtype=0), kernel="mfma") == fd.FD_ERR_UNSUPPORTED
+
+
+def test_strides_are_bounded_before_use():
+    """A stride above FD_MAX_STRIDE elements is rejected instead of overflowing
+    the byte products of the alignment checks; strides the layout does not use
+    are not looked at."""
+    import re
+
+    hdr = open(HEADER).read()
+    m = re.search(r"#define FD_MAX_STRIDE \(\(int64_t\)1 << (\d+)\)", hdr)
+    assert m
+    cap = 1 << int(m.group(1))
+    huge = (1 << 63) - 1
+    assert _status(contiguous_problem(q_stride_b=cap)) == fd.FD_OK
+    assert _status(contiguous_problem(q_stride_b=cap + 8)) == fd.FD_ERR_INVALID_ARG
+    for field in ("q_stride_b", "q_stride_h", "kv_stride_b", "kv_stride_h", "kv_stride_t"):
+        assert _status(contiguous_problem(**{field: huge})) == fd.FD_ERR_INVALID_ARG, field
+    for field in ("bt_stride_b", "pool_stride_page", "pool_stride_t", "pool_stride_h"):
+        assert _status(paged_problem(**{field: huge})) == fd.FD_ERR_INVALID_ARG, field
+        assert _status(contiguous_problem(**{field: huge})) == fd.FD_OK, field
+    assert _status(contiguous_problem(q_stride_q=huge)) == fd.FD_OK                  # single query
+    assert _status(contiguous_problem(q_len=2, q_stride_q=huge)) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(L=1000), force_chunk_tokens=100, force_splits=5) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(scale=float("nan"))) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(L=0)) == fd.FD_OK
