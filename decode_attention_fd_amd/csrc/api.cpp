@@ -309,7 +309,7 @@ FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_st
 FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,
                            int32_t num_states, int32_t head_dim, float* out, float* lse_out, void* stream) {
   if (ws_format != FD_WS_UML && ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
-  if (rows < 0 || rows > 0x7fffffff || num_states < 1 || num_states > 65535) return FD_ERR_INVALID_ARG;
+  if (rows < 0 || rows > 0x7fffffff - 4096 || num_states < 1 || num_states > 65535) return FD_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
   if (rows == 0) return FD_OK;
   if (!states || !stats || !out) return FD_ERR_INVALID_ARG;

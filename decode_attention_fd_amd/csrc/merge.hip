@@ -57,7 +57,7 @@ int launch_merge(const MergeParams& p, int head_dim, void* stream) {
   const int lpr = head_dim / 4;
   const int sg_log2 = split_groups_log2(p.S, lpr, 1, NT);
   const int rows_per_wg = NT / (lpr << sg_log2);
-  dim3 grid((p.BH + rows_per_wg - 1) / rows_per_wg);
+  dim3 grid((unsigned)(((int64_t)p.BH + rows_per_wg - 1) / rows_per_wg));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (head_dim == 128)
     hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(NT), 0, st, p, sg_log2);

@@ -294,7 +294,7 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
  * O = 0 and LSE = -inf. Layouts (float32, contiguous, device memory):
  * states [rows, num_states, head_dim], stats [rows, num_states] (OLSE) or
  * [rows, num_states, 2] (UML), out [rows, head_dim], lse_out [rows] or NULL.
- * head_dim in {64, 128}; 1 <= num_states <= 65535; 0 <= rows <= 2^31 - 1
+ * head_dim in {64, 128}; 1 <= num_states <= 65535; 0 <= rows <= 2^31 - 4097
  * (rows = 0 launches nothing). Inputs are read only; the caller owns every
  * buffer. Arguments are checked on the host before any launch. */
 FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,

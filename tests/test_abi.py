@@ -353,6 +353,7 @@ def test_merge_states_validation_without_gpu():
     assert st(7, *ok) == fd.FD_ERR_INVALID_ARG                             # format
     assert st(olse, 0x10000, 0x20000, -1, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
     assert st(olse, 0x10000, 0x20000, 1 << 31, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
+    assert st(olse, 0x10000, 0x20000, (1 << 31) - 4096, 4, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
     assert st(olse, 0x10000, 0x20000, 8, 0, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
     assert st(olse, 0x10000, 0x20000, 8, 65536, 128, 0x30000, None, None) == fd.FD_ERR_INVALID_ARG
     assert st(olse, 0x10000, 0x20000, 8, 4, 96, 0x30000, None, None) == fd.FD_ERR_UNSUPPORTED
