@@ -1,0 +1,20 @@
+// Tile geometry of the split kernels: the one definition that both the HIP
+// kernels (split_mfma.hip, split_valu.hip) and the host planner (api.cpp,
+// plan.cpp) read, so the planner's split boundaries always match the tiles
+// the kernels stream.
+#pragma once
+
+namespace fd {
+
+constexpr int kSplitWaves = 4;           // waves per split workgroup, both kernels
+constexpr int kMfmaTileTokens = 32;      // KV tokens per wave tile, MFMA kernel
+constexpr int kValuLoadsPerTile = 8;     // 16-byte load instructions per wave tile per tensor, VALU kernel
+
+// VALU kernel: a K/V row of head_dim elements is read by head_dim * elt / 16
+// lanes (16 bytes each), so one wave load instruction covers 64 / that many
+// rows, and a wave tile is kValuLoadsPerTile such instructions.
+constexpr int valu_tile_tokens_for(int head_dim, int elt_bytes) {
+  return kValuLoadsPerTile * (64 / (head_dim * elt_bytes / 16));
+}
+
+}  // namespace fd

@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include "fd_internal.h"
+#include "geometry.h"
 #include "merge_rows.h"
 #include "balance.h"
 
@@ -33,9 +34,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int NW = 4;
+constexpr int NW = kSplitWaves;
 constexpr int FUSED_BATCH = 8;   // splits per lane in flight in the fused merge
-constexpr int U = 8;      // load instructions per tile per tensor
+constexpr int U = kValuLoadsPerTile;   // load instructions per tile per tensor
 constexpr float LN2 = 0.69314718055994530942f;
 
 template <int CTRL>
@@ -116,6 +117,7 @@ template <int D, typename T> struct VGeo {
   static constexpr int RPI = 64 / LPR;       // rows per load instruction
   static constexpr int TT = U * RPI;         // tokens per wave tile
   static constexpr int ELT = sizeof(T);
+  static_assert(TT == valu_tile_tokens_for(D, sizeof(T)), "planner and kernel tile sizes differ");
 };
 
 template <int D, typename T, int G> struct VSmem {
@@ -369,8 +371,12 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   const int b = blockIdx.z;
   int seq_len = p.seq_lens[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
-  const int start = s * p.chunk;
-  const int end = min(start + p.chunk, seq_len);
+  // Split s covers [s*chunk, s*chunk + chunk) clamped to the sequence; formed
+  // in 64 bits (the plan bounds S*chunk by INT32_MAX, but a start past the
+  // sequence must never wrap to a negative token index).
+  const int64_t s0 = (int64_t)s * p.chunk;
+  const int start = (int)(s0 < seq_len ? s0 : seq_len);
+  const int end = (int)(s0 + p.chunk < seq_len ? s0 + p.chunk : seq_len);
   const bool direct = p.fused && p.S == 1;    // fused call with one split: write out/lse directly
   valu_piece<D, T, G, PAGED>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
   if (p.fused && !direct) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, p.S);
@@ -473,12 +479,6 @@ int occupancy_split_valu(int head_dim, int kv_dtype, int layout, int group_tpl, 
     if (kv_dtype == FD_DTYPE_BF16) return occupancy_t<64, __bf16>(paged, group_tpl, out);
   }
   return (int)hipErrorInvalidValue;
-}
-
-int valu_tile_tokens(int head_dim, int kv_dtype) {
-  const int epl = kv_dtype == FD_DTYPE_F32 ? 4 : 8;
-  const int lpr = head_dim / epl;
-  return U * (64 / lpr);
 }
 
 }  // namespace fd

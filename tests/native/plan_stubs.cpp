@@ -9,8 +9,4 @@ int launch_split_mfma(const SplitParams&, int, int, int, void*) { return 1; }
 int launch_split_valu(const SplitParams&, int, int, int, int, void*) { return 1; }
 int occupancy_split_mfma(int, int, int, int, int* o) { *o = 1; return 0; }
 int occupancy_split_valu(int, int, int, int, int* o) { *o = 1; return 0; }
-int valu_tile_tokens(int head_dim, int kv_dtype) {
-  const int epl = kv_dtype == FD_DTYPE_F32 ? 4 : 8;
-  return 8 * (64 / (head_dim / epl));   // the VALU kernel's tile: 8 loads per lane per tensor
-}
 }
