@@ -105,8 +105,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.fd_decode_fused.restype = ctypes.c_int
-        L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                               ctypes.c_void_p, ctypes.c_void_p]
+        L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                               ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge.restype = ctypes.c_int
         L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -226,6 +226,76 @@ def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_sp
     return plan
 
 
+def _rows(plan: Plan) -> int:
+    pr = plan.prob
+    return pr.batch * (pr.q_len if pr.q_len > 1 else 1) * pr.num_q_heads
+
+
+def _device_of(tensors) -> torch.device:
+    """The one GPU every given tensor lives on; raises otherwise (the kernels
+    dereference every pointer on that device)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be GPU tensors, got {dev}")
+    return dev
+
+
+def _check_f32(t: torch.Tensor, name: str, numel: Optional[int] = None, at_least: bool = False) -> None:
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if numel is not None and (t.numel() < numel if at_least else t.numel() != numel):
+        raise ValueError(f"{name} holds {t.numel()} elements, the plan needs {'at least ' if at_least else ''}{numel}")
+
+
+def _check_inputs(plan: Plan, q, k, v, seq_lens, block_table) -> None:
+    """The launch's tensors against the plan's problem: dtypes, shapes and
+    strides as planned, seq_lens int32 with an entry per sequence, the block
+    table present exactly for paged problems and wide enough."""
+    pr = plan.prob
+    dtype_of = {c: t for t, c in DTYPES.items()}
+    if q.dtype != dtype_of.get(pr.q_dtype) or k.dtype != dtype_of.get(pr.kv_dtype) or v.dtype != k.dtype:
+        raise ValueError("q/K/V dtypes differ from the plan's problem")
+    if q.dim() == 4:
+        ql = pr.q_len if pr.q_len > 1 else 1
+        want_q = ((pr.batch, ql, pr.num_q_heads, pr.head_dim), (pr.q_stride_b, pr.q_stride_q, pr.q_stride_h))
+        got_q = (tuple(q.shape), tuple(q.stride()[:3]))
+    else:
+        want_q = ((pr.batch, pr.num_q_heads, pr.head_dim), (pr.q_stride_b, pr.q_stride_h))
+        got_q = (tuple(q.shape), tuple(q.stride()[:2]))
+    if got_q != want_q or q.stride(-1) != 1:
+        raise ValueError(f"q shape/strides {got_q} differ from the plan's {want_q}")
+    if pr.layout == LAYOUT_PAGED:
+        want_kv = ((pr.num_pages, pr.page_size, pr.num_kv_heads, pr.head_dim),
+                   (pr.pool_stride_page, pr.pool_stride_t, pr.pool_stride_h, 1))
+        if block_table is None:
+            raise ValueError("a paged plan needs block_table")
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] < pr.batch
+                or block_table.shape[1] < pr.max_pages_per_seq or block_table.stride(1) != 1
+                or block_table.stride(0) != pr.bt_stride_b):
+            raise ValueError("block_table must be int32 [>= B, >= max_pages_per_seq] with the planned row stride")
+    else:
+        want_kv = ((pr.batch, pr.num_kv_heads, pr.kv_capacity, pr.head_dim),
+                   (pr.kv_stride_b, pr.kv_stride_h, pr.kv_stride_t, 1))
+        if block_table is not None:
+            raise ValueError("a contiguous plan takes no block_table")
+    for name, t in (("K", k), ("V", v)):
+        if (tuple(t.shape), tuple(t.stride())) != want_kv:
+            raise ValueError(f"{name} shape/strides {(tuple(t.shape), tuple(t.stride()))} differ from the plan's {want_kv}")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or seq_lens.stride(0) != 1 or seq_lens.numel() < pr.batch:
+        raise ValueError("seq_lens must be a contiguous int32 vector with one entry per sequence")
+    _device_of([q, k, v, seq_lens, block_table])
+
+
+def _check_outputs(plan: Plan, out, lse) -> None:
+    rows = _rows(plan)
+    _check_f32(out, "out", rows * plan.prob.head_dim)
+    if lse is not None:
+        _check_f32(lse, "lse", rows)
+
+
 def workspace(plan: Plan, device) -> Tuple[torch.Tensor, torch.Tensor]:
     """Allocate the fp32 workspace the plan asks for: (ws_o [B,(q_len,)Hq,S,D], ws_stats)."""
     pr = plan.prob
@@ -239,6 +309,10 @@ def workspace(plan: Plan, device) -> Tuple[torch.Tensor, torch.Tensor]:
 
 def fd_decode_split(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, block_table=None, stream=None) -> None:
     """Launch the split kernel on ``stream`` (default: torch's current stream)."""
+    _check_inputs(plan, q, k, v, seq_lens, block_table)
+    _device_of([q, ws_o, ws_stats])
+    _check_f32(ws_o, "ws_o")
+    _check_f32(ws_stats, "ws_stats")
     a = Args(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_table))
     st = lib().fd_decode_split(ctypes.byref(plan), ctypes.byref(a), _ptr(ws_o), ws_o.numel() * ws_o.element_size(),
                                _ptr(ws_stats), ws_stats.numel() * ws_stats.element_size(), _stream_handle(stream))
@@ -253,10 +327,13 @@ def counters(plan: Plan, device) -> torch.Tensor:
 def fd_decode_fused(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, ctr, out, lse=None, block_table=None,
                     stream=None) -> None:
     """Split kernel with the merge fused in: writes out (and lse) in one launch."""
-    if out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor")
+    _check_inputs(plan, q, k, v, seq_lens, block_table)
+    _device_of([q, ws_o, ws_stats, ctr, out, lse])
+    _check_f32(ws_o, "ws_o")
+    _check_f32(ws_stats, "ws_stats")
+    _check_outputs(plan, out, lse)
+    if ctr.dtype not in (torch.int32, torch.uint32) or not ctr.is_contiguous():
+        raise ValueError("counters must be a contiguous 32-bit integer tensor")
     a = Args(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_table))
     st = lib().fd_decode_fused(ctypes.byref(plan), ctypes.byref(a), _ptr(ws_o), ws_o.numel() * ws_o.element_size(),
                                _ptr(ws_stats), ws_stats.numel() * ws_stats.element_size(), _ptr(ctr),
@@ -266,12 +343,12 @@ def fd_decode_fused(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, ctr, out, lse
 
 def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:
     """Launch the merge kernel: out [B,Hq,D] fp32 (contiguous), lse [B,Hq] fp32 or None."""
-    if out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor")
-    st = lib().fd_merge(ctypes.byref(plan), _ptr(ws_o), _ptr(ws_stats), _ptr(out), _ptr(lse),
-                        _stream_handle(stream))
+    _check_f32(ws_o, "ws_o")
+    _check_f32(ws_stats, "ws_stats")
+    _check_outputs(plan, out, lse)
+    _device_of([ws_o, ws_stats, out, lse])
+    st = lib().fd_merge(ctypes.byref(plan), _ptr(ws_o), ws_o.numel() * 4, _ptr(ws_stats), ws_stats.numel() * 4,
+                        _ptr(out), _ptr(lse), _stream_handle(stream))
     _check(st, "fd_merge")
 
 
@@ -281,6 +358,7 @@ def fd_merge_states(states, stats, out=None, lse_out=None, *, ws_format: str = "
     (olse: natural-log LSE) or [..., S, 2] (uml: m, l). Returns (out [..., D],
     lse_out [...]), allocating them when not given."""
     fmt = WS_FORMATS[ws_format]
+    _device_of([states, stats, out, lse_out])
     if states.dtype != torch.float32 or stats.dtype != torch.float32:
         raise ValueError("states and stats must be float32")
     if not states.is_contiguous() or not stats.is_contiguous():
@@ -312,6 +390,9 @@ READ_PROBE_SINK_BYTES = 512 * 256 * 4
 def fd_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """Launch the streaming-read probe over ``buf`` (device, bytes a multiple of
     16); ``sink`` is an int32/uint32 device tensor of READ_PROBE_SINK_BYTES."""
+    _device_of([buf, sink])
+    if not buf.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("buf and sink must be contiguous")
     st = lib().fd_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                              sink.numel() * sink.element_size(), _stream_handle(stream))
     _check(st, "fd_read_probe")

@@ -9,10 +9,10 @@
 #include <mutex>
 
 #include "fd_internal.h"
+#include "geometry.h"
 
 namespace fd {
 
-int valu_tile_tokens(int head_dim, int kv_dtype);          // split_valu.hip
 int occupancy_split_mfma(int head_dim, int kv_dtype, int layout, int nct, int* out);
 int occupancy_split_valu(int head_dim, int kv_dtype, int layout, int group_tpl, int* out);
 
@@ -23,10 +23,10 @@ int occupancy_split(int kernel, int head_dim, int kv_dtype, int layout, int vari
 }
 
 int split_tile_tokens(int kernel, int head_dim, int kv_dtype) {
-  return kernel == FD_KERNEL_MFMA ? 32 : valu_tile_tokens(head_dim, kv_dtype);
+  return kernel == FD_KERNEL_MFMA ? kMfmaTileTokens : valu_tile_tokens_for(head_dim, dtype_size(kv_dtype));
 }
 
-int split_waves_per_wg(int /*kernel*/) { return 4; }
+int split_waves_per_wg(int /*kernel*/) { return kSplitWaves; }
 
 // Resident split workgroups per CU of each compiled variant, generated at build
 // time from the compiler's resource usage (VGPRs and LDS per workgroup); used
@@ -286,19 +286,24 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
   return launch_split(plan, p, stream);
 }
 
-FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats, float* out, float* lse,
-                    void* stream) {
+FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, size_t ws_o_bytes, const float* ws_stats,
+                    size_t ws_stats_bytes, float* out, float* lse, void* stream) {
   int st = check_plan(plan);
   if (st != FD_OK) return st;
   if (!ws_o || !ws_stats || !out) return FD_ERR_INVALID_ARG;
   if (!aligned(ws_o, 16) || !aligned(ws_stats, 8) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
     return FD_ERR_ALIGNMENT;
+  if (ws_o_bytes < (size_t)plan->ws_o_bytes || ws_stats_bytes < (size_t)plan->ws_stats_bytes)
+    return FD_ERR_WORKSPACE;
+  // validate_problem (through check_plan) bounded the rows by FD_MAX_ROWS.
+  const int64_t rows = (int64_t)plan->prob.batch * (plan->prob.q_len > 1 ? plan->prob.q_len : 1) *
+                       plan->prob.num_q_heads;
   MergeParams p;
   p.ws_o = ws_o;
   p.ws_stats = ws_stats;
   p.out = out;
   p.lse = lse;
-  p.BH = plan->prob.batch * (plan->prob.q_len > 1 ? plan->prob.q_len : 1) * plan->prob.num_q_heads;
+  p.BH = (int32_t)rows;
   p.S = plan->num_splits;
   p.ws_format = plan->ws_format;
   int err = launch_merge(p, plan->prob.head_dim, stream);
@@ -309,7 +314,7 @@ FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_st
 FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,
                            int32_t num_states, int32_t head_dim, float* out, float* lse_out, void* stream) {
   if (ws_format != FD_WS_UML && ws_format != FD_WS_OLSE) return FD_ERR_INVALID_ARG;
-  if (rows < 0 || rows > 0x7fffffff - 4096 || num_states < 1 || num_states > 65535) return FD_ERR_INVALID_ARG;
+  if (rows < 0 || rows > FD_MAX_ROWS || num_states < 1 || num_states > 65535) return FD_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
   if (rows == 0) return FD_OK;
   if (!states || !stats || !out) return FD_ERR_INVALID_ARG;

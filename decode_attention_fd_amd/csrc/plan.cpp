@@ -29,10 +29,6 @@ namespace {
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-bool eligible(int s, int64_t n_blocks) {
-  return s == 1 || cdiv64(n_blocks, s) != cdiv64(n_blocks, s - 1);
-}
-
 double wave_eff(int64_t work, int s, int64_t slots) {
   double w = (double)work * (double)s / (double)slots;
   return w / ceil(w);
@@ -43,7 +39,15 @@ double ws_ratio(int s, int g, int d, int elt, int64_t max_len) {
   return (2.0 * s * g * (d + 2) * 4.0) / (2.0 * (double)max_len * d * elt);
 }
 
-// kanthi.in §6 rule; with budget < 0 no traffic bound is applied.
+// The split-count rule of kanthi.in §6, organised by blocks per split. A split
+// count s matters only through q = cdiv(n_blocks, s), the blocks each split
+// streams, so the candidates are the fewest splits that give each distinct q:
+// s = 1, then s' = cdiv(n_blocks, q - 1) after a count with q blocks, up to
+// cap = min(max_splits, slots, n_blocks). The answer is S = 1 when the work
+// units alone fill 80 % of the slots; otherwise the smallest candidate whose
+// last-wave efficiency reaches `threshold` times the best candidate's. With
+// budget >= 0, candidates above 1 whose workspace traffic exceeds the budget
+// are left out (the overhead check at the end of §6).
 int split_rule(int64_t work, int64_t slots, int64_t n_blocks, int max_splits, int g, int d, int elt,
                int64_t max_len, double budget, double threshold) {
   if ((double)work >= 0.8 * (double)slots) return 1;
@@ -51,19 +55,24 @@ int split_rule(int64_t work, int64_t slots, int64_t n_blocks, int max_splits, in
   if (slots < cap) cap = slots;
   if (n_blocks < cap) cap = n_blocks;
   if (cap <= 1) return 1;
+  // Visit the candidates in increasing order; f(s, eff) returns true to stop.
+  auto visit = [&](auto&& f) {
+    for (int64_t s = 1; s <= cap;) {
+      if ((s == 1 || budget < 0.0 || ws_ratio((int)s, g, d, elt, max_len) <= budget) &&
+          f((int)s, wave_eff(work, (int)s, slots)))
+        return (int)s;
+      const int64_t q = cdiv64(n_blocks, s);
+      if (q <= 1) break;
+      s = cdiv64(n_blocks, q - 1);
+    }
+    return 1;
+  };
   double best = 0.0;
-  for (int s = 1; s <= cap; ++s) {
-    if (!eligible(s, n_blocks)) continue;
-    if (s > 1 && budget >= 0.0 && ws_ratio(s, g, d, elt, max_len) > budget) continue;
-    double e = wave_eff(work, s, slots);
-    if (e > best) best = e;
-  }
-  for (int s = 1; s <= cap; ++s) {
-    if (!eligible(s, n_blocks)) continue;
-    if (s > 1 && budget >= 0.0 && ws_ratio(s, g, d, elt, max_len) > budget) continue;
-    if (wave_eff(work, s, slots) >= threshold * best) return s;
-  }
-  return 1;
+  visit([&](int, double e) {
+    best = e > best ? e : best;
+    return false;
+  });
+  return visit([&](int, double e) { return e >= threshold * best; });
 }
 
 }  // namespace
@@ -78,6 +87,9 @@ int validate_problem(const fd_problem* p) {
   if (p->head_dim != 64 && p->head_dim != 128) return FD_ERR_UNSUPPORTED;
   if (p->q_dtype != p->kv_dtype) return FD_ERR_UNSUPPORTED;
   if (p->max_seq_len < 0) return FD_ERR_INVALID_ARG;
+  if (p->q_len < 0 || p->q_len > 8) return FD_ERR_UNSUPPORTED;
+  // Output rows B * q_len * Hq index 32-bit merge grids.
+  if ((int64_t)p->batch * (p->q_len > 1 ? p->q_len : 1) * p->num_q_heads > FD_MAX_ROWS) return FD_ERR_UNSUPPORTED;
   if (!(isfinite(p->scale))) return FD_ERR_INVALID_ARG;
   const int64_t elt = dtype_size(p->kv_dtype);
   const int64_t D = p->head_dim;
@@ -96,7 +108,6 @@ int validate_problem(const fd_problem* p) {
     if (v > FD_MAX_STRIDE) return FD_ERR_INVALID_ARG;
   if (p->q_stride_h < D || p->q_stride_b < 0) return FD_ERR_INVALID_ARG;
   if ((p->q_stride_h * elt) % 16 || (p->q_stride_b * elt) % 16) return FD_ERR_ALIGNMENT;
-  if (p->q_len < 0 || p->q_len > 8) return FD_ERR_UNSUPPORTED;
   if (p->q_len > 1) {
     if (p->q_stride_q < 0) return FD_ERR_INVALID_ARG;
     if ((p->q_stride_q * elt) % 16) return FD_ERR_ALIGNMENT;
@@ -341,6 +352,9 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
     S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
   }
   if (S < 1 || S > 65535 || chunk < 1 || chunk > 0x7fffffff) return FD_ERR_UNSUPPORTED;
+  // Uniform splits start at s * chunk, a 32-bit token index in the kernels:
+  // every split boundary must fit (forced counts and chunks can ask for more).
+  if (nwg == 0 && S * chunk > (int64_t)0x7fffffff) return FD_ERR_UNSUPPORTED;
   if (slots == 0) slots = (int64_t)o->num_cus * o->wgs_per_cu;
 
   out->magic = FD_PLAN_MAGIC;

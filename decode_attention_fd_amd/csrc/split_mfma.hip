@@ -42,6 +42,7 @@
 #include <math.h>
 
 #include "fd_internal.h"
+#include "geometry.h"
 #include "merge_rows.h"
 #include "balance.h"
 
@@ -68,9 +69,9 @@ template <> struct Mma<__bf16> {
   }
 };
 
-constexpr int NW = 4;    // waves per workgroup
+constexpr int NW = kSplitWaves;   // waves per workgroup
 constexpr int FUSED_BATCH = 16;   // splits per lane in flight in the fused merge
-constexpr int TT = 32;   // tokens per wave tile
+constexpr int TT = kMfmaTileTokens;   // tokens per wave tile
 constexpr float LN2 = 0.69314718055994530942f;
 
 template <int D> struct Geo {
@@ -442,8 +443,12 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   const int b = blockIdx.z;
   int seq_len = p.seq_lens[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
-  const int start = s * p.chunk;
-  const int end = min(start + p.chunk, seq_len);
+  // Split s covers [s*chunk, s*chunk + chunk) clamped to the sequence; formed
+  // in 64 bits (the plan bounds S*chunk by INT32_MAX, but a start past the
+  // sequence must never wrap to a negative token index).
+  const int64_t s0 = (int64_t)s * p.chunk;
+  const int start = (int)(s0 < seq_len ? s0 : seq_len);
+  const int end = (int)(s0 + p.chunk < seq_len ? s0 + p.chunk : seq_len);
   const bool direct = p.fused && p.S == 1;
   if (end > start)
     split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);

@@ -136,6 +136,11 @@ typedef enum {
  * FD_ERR_INVALID_ARG. */
 #define FD_MAX_STRIDE ((int64_t)1 << 40)
 
+/* Largest number of output rows B * q_len * Hq of a problem (and of
+ * fd_merge_states): merge grids are indexed in 32 bits. A larger problem is
+ * FD_ERR_UNSUPPORTED. */
+#define FD_MAX_ROWS ((int64_t)0x7fffffff - 4096)
+
 /* Default start-up cost of one balanced piece, in KV tokens. */
 #define FD_DEFAULT_PIECE_COST_TOKENS 512
 
@@ -243,7 +248,9 @@ typedef struct {
 /* Choose the split count, chunk, kernel and workspace sizes for a problem
  * (kanthi.in §6; xuujii §07 "choose a split plan for the current batch/head/
  * length"). Host only; touches the device only when opts->num_cus == 0.
- * opts may be NULL (all defaults). */
+ * opts may be NULL (all defaults). A uniform plan whose split boundaries
+ * would pass 2^31 - 1 tokens (num_splits * chunk_tokens > INT32_MAX, e.g. a
+ * forced split count times a forced chunk) is FD_ERR_UNSUPPORTED. */
 FD_API int fd_plan(const fd_problem* prob, const fd_plan_opts* opts, fd_plan_t* out);
 
 /* Split kernel: for every (b, kv head, split) one workgroup streams the split's
@@ -259,9 +266,12 @@ FD_API int fd_decode_split(const fd_plan_t* plan, const fd_args* args,
  * w_s = e^{m_s - max_s m_s} (UML) or O = sum_s w_s o_s / sum_s w_s with
  * w_s = e^{lse_s - max lse} (OLSE); LSE = max + ln(sum) (kanthi.in §2 stable
  * form, §4 kernel 2; xuujii §04). Splits with m = -inf weigh 0.
+ * ws_o / ws_stats: the workspace fd_decode_split wrote, of ws_o_bytes /
+ * ws_stats_bytes bytes; either smaller than the plan's ws_o_bytes /
+ * ws_stats_bytes is FD_ERR_WORKSPACE (nothing is launched).
  * out: float [B, Hq, D] contiguous; lse: float [B, Hq] or NULL. */
-FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, const float* ws_stats,
-                    float* out, float* lse, void* stream);
+FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, size_t ws_o_bytes, const float* ws_stats,
+                    size_t ws_stats_bytes, float* out, float* lse, void* stream);
 
 /* Split kernel with the merge fused in: as fd_decode_split, and in addition the
  * workgroup that finishes last for each (sequence, KV head) merges that
@@ -294,7 +304,7 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
  * O = 0 and LSE = -inf. Layouts (float32, contiguous, device memory):
  * states [rows, num_states, head_dim], stats [rows, num_states] (OLSE) or
  * [rows, num_states, 2] (UML), out [rows, head_dim], lse_out [rows] or NULL.
- * head_dim in {64, 128}; 1 <= num_states <= 65535; 0 <= rows <= 2^31 - 4097
+ * head_dim in {64, 128}; 1 <= num_states <= 65535; 0 <= rows <= FD_MAX_ROWS
  * (rows = 0 launches nothing). Inputs are read only; the caller owns every
  * buffer. Arguments are checked on the host before any launch. */
 FD_API int fd_merge_states(int ws_format, const float* states, const float* stats, int64_t rows,

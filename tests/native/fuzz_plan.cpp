@@ -96,6 +96,11 @@ int main(int argc, char** argv) {
       o.wgs_per_cu = rng() % 3;
       o.force_splits = rng() % 4 == 0 ? 1 + rng() % 300 : 0;
       o.force_chunk_tokens = rng() % 6 == 0 ? 1 + rng() % 9000 : 0;
+      if (rng() % 16 == 0) {                 // forced pairs near the 32-bit token bound
+        o.force_splits = 1 + (int32_t)(rng() % 65535);
+        o.force_chunk_tokens = 1 << (10 + rng() % 11);
+        if (p.layout == FD_LAYOUT_PAGED) o.force_chunk_tokens = 0;
+      }
       o.ws_format = rng() % 2; o.kernel = 0; o.heuristic = rng() % 3;
       o.max_splits = rng() % 4 == 0 ? 1 + rng() % 300 : 0;
       o.overhead_budget = rng() % 4 == 0 ? (float)(rng() % 2000) * 1e-3f : 0.0f;
@@ -109,6 +114,11 @@ int main(int argc, char** argv) {
       ++ok;
       if (pl.num_splits < 1 || pl.grid_x < 1 || pl.ws_o_bytes < 0 || pl.ws_stats_bytes < 0) {
         printf("iter %ld: odd plan S=%d grid=%d\n", it, pl.num_splits, pl.grid_x);
+        return 1;
+      }
+      // uniform split s starts at token s * chunk, a 32-bit index on the device
+      if (pl.schedule == FD_SCHEDULE_UNIFORM && (int64_t)pl.num_splits * pl.chunk_tokens > INT32_MAX) {
+        printf("iter %ld: split boundaries overflow: S=%d chunk=%d\n", it, pl.num_splits, pl.chunk_tokens);
         return 1;
       }
     } else ++bad;

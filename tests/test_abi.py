@@ -300,6 +300,40 @@ def test_strides_are_bounded_before_use():
     assert _status(contiguous_problem(L=0)) == fd.FD_OK
 
 
+def test_split_boundaries_fit_32_bits():
+    """Uniform split s starts at token s * chunk, a 32-bit index on the device:
+    a forced split count times a forced (or page-rounded) chunk past 2^31 - 1
+    is refused, and the largest plan that fits is accepted."""
+    big = contiguous_problem(Hq=8, Hkv=8, L=1000)
+    assert _status(big, force_splits=65535, force_chunk_tokens=65536) == fd.FD_ERR_UNSUPPORTED
+    assert _status(big, force_splits=32768, force_chunk_tokens=65536) == fd.FD_ERR_UNSUPPORTED   # 2^31 exactly
+    p = fd.fd_plan(big, num_cus=256, force_splits=32767, force_chunk_tokens=65536)
+    assert p.num_splits * p.chunk_tokens == 32767 * 65536 <= (1 << 31) - 1
+    # paged: 2^20-token pages round every chunk up to a page
+    paged = paged_problem(L=1 << 20, page=1 << 20, max_pages_per_seq=1)
+    assert _status(paged, force_splits=4096) == fd.FD_ERR_UNSUPPORTED
+    assert _status(paged, force_splits=2047) == fd.FD_OK
+
+
+def test_output_rows_are_bounded():
+    """B * q_len * Hq output rows index 32-bit merge grids: more than FD_MAX_ROWS
+    is refused by the planner."""
+    import re
+
+    hdr = open(HEADER).read()
+    m = re.search(r"#define FD_MAX_ROWS \(\(int64_t\)0x7fffffff - (\d+)\)", hdr)
+    assert m
+    max_rows = 0x7FFFFFFF - int(m.group(1))
+    # 4096 KV heads x 16 query heads each: 65536 rows per sequence
+    p = contiguous_problem(B=max_rows // 65536 + 1, Hq=65536, Hkv=4096, L=64)
+    assert _status(p) == fd.FD_ERR_UNSUPPORTED
+    p.batch = max_rows // 65536
+    assert _status(p) == fd.FD_OK
+    p = contiguous_problem(B=max_rows // (8 * 8192) + 1, Hq=8192, Hkv=4096, L=64, q_len=8,
+                           q_stride_q=8192 * 128, q_stride_b=8 * 8192 * 128)
+    assert _status(p) == fd.FD_ERR_UNSUPPORTED                         # g * q_len = 16, rows include q_len
+
+
 def test_plan_resolves_scale_and_workspace():
     p = fd.fd_plan(contiguous_problem(B=2, Hq=16, Hkv=8, D=64, L=500), num_cus=256)
     assert abs(p.scale - 1 / 8) < 1e-7
@@ -334,11 +368,61 @@ def test_decode_and_merge_validation_without_gpu():
     bad.magic = 0
     assert _split_status(bad, good) == fd.FD_ERR_BAD_PLAN
     L = fd.lib()
-    assert L.fd_merge(ctypes.byref(bad), 4096, 8192, 4096, None, None) == fd.FD_ERR_BAD_PLAN
-    assert L.fd_merge(ctypes.byref(plan), None, 8192, 4096, None, None) == fd.FD_ERR_INVALID_ARG
-    assert L.fd_merge(ctypes.byref(plan), 4096, 8192, 4100, None, None) == fd.FD_ERR_ALIGNMENT
+    big = 1 << 40
+
+    def merge(pl, ws_o=4096, ws_o_bytes=big, ws_st=8192, ws_st_bytes=big, out=4096):
+        return L.fd_merge(ctypes.byref(pl), ws_o, ws_o_bytes, ws_st, ws_st_bytes, out, None, None)
+
+    assert merge(bad) == fd.FD_ERR_BAD_PLAN
+    assert merge(plan, ws_o=None) == fd.FD_ERR_INVALID_ARG
+    assert merge(plan, out=None) == fd.FD_ERR_INVALID_ARG
+    assert merge(plan, out=4100) == fd.FD_ERR_ALIGNMENT
+    # a workspace shorter than the plan's is refused before any launch
+    assert merge(plan, ws_o_bytes=plan.ws_o_bytes - 4) == fd.FD_ERR_WORKSPACE
+    assert merge(plan, ws_st_bytes=plan.ws_stats_bytes - 4) == fd.FD_ERR_WORKSPACE
+    assert merge(plan, ws_o_bytes=0, ws_st_bytes=0) == fd.FD_ERR_WORKSPACE
     paged = fd.fd_plan(paged_problem(), num_cus=256)
     assert _split_status(paged, good) == fd.FD_ERR_INVALID_ARG          # no block table
+
+
+def test_binding_checks_tensors_against_the_plan():
+    """The Python launch wrappers refuse, before any C call, tensors that do not
+    match the plan: host tensors, int64 lengths (read as int32 pairs they would
+    give wrong lengths), a missing or short block table, K/V of another shape,
+    and outputs or workspaces of the wrong size or type."""
+    B, Hq, Hkv, D, T = 2, 8, 2, 128, 64
+    q = torch.zeros(B, Hq, D, dtype=torch.float16)
+    k = torch.zeros(B, Hkv, T, D, dtype=torch.float16)
+    sl = torch.tensor([64, 5], dtype=torch.int32)
+    plan = fd.fd_plan(fd.problem_for(q, k, k, sl), num_cus=256)
+    ws_o, ws_st = torch.zeros(1), torch.zeros(1)
+
+    def msg(fn):
+        with pytest.raises(ValueError) as e:
+            fn()
+        return str(e.value)
+
+    assert "GPU" in msg(lambda: fd.fd_decode_split(plan, q, k, k, sl, ws_o, ws_st))
+    assert "seq_lens" in msg(lambda: fd.fd_decode_split(plan, q, k, k, sl.to(torch.int64), ws_o, ws_st))
+    assert "seq_lens" in msg(lambda: fd.fd_decode_split(plan, q, k, k, sl[:1], ws_o, ws_st))
+    assert "K shape" in msg(lambda: fd.fd_decode_split(plan, q, k[:, :, :32], k, sl, ws_o, ws_st))
+    assert "dtypes" in msg(lambda: fd.fd_decode_split(plan, q.float(), k, k, sl, ws_o, ws_st))
+    assert "q shape" in msg(lambda: fd.fd_decode_split(plan, q[:1], k, k, sl, ws_o, ws_st))
+    assert "block_table" in msg(lambda: fd.fd_decode_split(plan, q, k, k, sl, ws_o, ws_st,
+                                                           torch.zeros(B, 4, dtype=torch.int32)))
+    pool = torch.zeros(8, 16, Hkv, D, dtype=torch.float16)
+    bt = torch.zeros(B, 4, dtype=torch.int32)
+    paged = fd.fd_plan(fd.problem_for(q, pool, pool, sl, bt), num_cus=256)
+    assert "block_table" in msg(lambda: fd.fd_decode_split(paged, q, pool, pool, sl, ws_o, ws_st))
+    assert "block_table" in msg(lambda: fd.fd_decode_split(paged, q, pool, pool, sl, ws_o, ws_st, bt[:1]))
+    assert "block_table" in msg(lambda: fd.fd_decode_split(paged, q, pool, pool, sl, ws_o, ws_st, bt.long()))
+    out = torch.zeros(B, Hq, D)
+    lse = torch.zeros(B, Hq)
+    fd._check_outputs(plan, out, lse)
+    assert "out" in msg(lambda: fd._check_outputs(plan, out[:1], lse))
+    assert "lse" in msg(lambda: fd._check_outputs(plan, out, lse.double()))
+    assert "out" in msg(lambda: fd._check_outputs(plan, out.transpose(0, 1), lse))
+    assert "ws_o" in msg(lambda: fd.fd_merge(plan, ws_o.double(), ws_st, out, lse))
 
 
 def test_merge_states_validation_without_gpu():

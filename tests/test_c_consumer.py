@@ -3,6 +3,7 @@ include/fd.h, links libfd.so and plans the 128k-token GQA step, an invalid
 problem and a balanced ragged batch. Its output must equal what the Python
 binding gets from the same calls, and the struct sizes it sees must equal the
 library's own."""
+import ctypes
 import os
 import shutil
 import subprocess
@@ -14,6 +15,7 @@ import decode_attention_fd_amd as fd
 from tests.conftest import ROOT
 
 PROGRAM = r"""
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -69,6 +71,23 @@ int main(void) {
   o.host_seq_lens = lens;
   o.num_host_seq_lens = 6;
   show("balanced", fd_plan(&p, &o, &pl), &pl);
+
+  /* a workspace one float short of the plan's: refused before any launch */
+  contiguous(&p, 1, 64, 8, 128, 128000);
+  memset(&o, 0, sizeof o);
+  o.num_cus = 256;
+  fd_plan(&p, &o, &pl);
+  {
+    int st = fd_merge(&pl, (const float*)(uintptr_t)4096, (size_t)pl.ws_o_bytes - 4,
+                      (const float*)(uintptr_t)8192, (size_t)pl.ws_stats_bytes, (float*)(uintptr_t)4096, NULL, NULL);
+    printf("merge_short status %d %s\n", st, fd_status_str(st));
+  }
+
+  /* split boundaries past 2^31 - 1 tokens */
+  contiguous(&p, 1, 8, 8, 128, 1000);
+  o.force_splits = 65535;
+  o.force_chunk_tokens = 65536;
+  show("overflow", fd_plan(&p, &o, &pl), &pl);
   return 0;
 }
 """
@@ -103,6 +122,11 @@ def _python_side() -> list:
     lines.append(show("balanced", lambda: fd.fd_plan(contiguous(6, 32, 8, 128, 5000), num_cus=256,
                                                      schedule="balanced",
                                                      host_seq_lens=[3000, 17, 0, 2200, 5000, 900])))
+    pl = fd.fd_plan(contiguous(1, 64, 8, 128, 128000), num_cus=256)
+    st = L.fd_merge(ctypes.byref(pl), 4096, pl.ws_o_bytes - 4, 8192, pl.ws_stats_bytes, 4096, None, None)
+    lines.append(f"merge_short status {st} {fd.status_str(st)}")
+    lines.append(show("overflow", lambda: fd.fd_plan(contiguous(1, 8, 8, 128, 1000), num_cus=256,
+                                                     force_splits=65535, force_chunk_tokens=65536)))
     return lines
 
 
@@ -118,3 +142,5 @@ def test_plain_c_program_sees_the_same_library(tmp_path):
     assert out == _python_side()
     assert out[2].startswith("gqa status 0 ") and out[3].startswith("bad status 1 ")
     assert " schedule 2 " in out[4]
+    assert out[5] == f"merge_short status {fd.FD_ERR_WORKSPACE} {fd.status_str(fd.FD_ERR_WORKSPACE)}"
+    assert out[6].startswith(f"overflow status {fd.FD_ERR_UNSUPPORTED} ")
