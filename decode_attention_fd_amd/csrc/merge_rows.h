@@ -294,7 +294,14 @@ __device__ __forceinline__ void ws_store(float* p, float v, bool coherent) {
 template <int D, int NTHREADS, int NB>
 __device__ __forceinline__ void fused_group_merge(const SplitParams& p, int b, int kvh, int expected) {
   __shared__ int s_last;
+  // Publication: the state stores are device-scope (sc1) stores, which write
+  // through to the device's coherence point, so once the wait below has seen
+  // them complete they are visible to sc1 loads from any CU of any XCD. The
+  // two compiler-only fences keep the stores before the wait and the counter
+  // atomic after it (the wait intrinsic itself claims no memory effects).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);            // this thread's state stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old = __hip_atomic_fetch_add(p.counters + (int64_t)b * p.Hkv + kvh, 1u, __ATOMIC_RELAXED,

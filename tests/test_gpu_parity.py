@@ -344,6 +344,51 @@ def test_fused_repeated_calls_reset_counters():
     assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
 
 
+@pytest.mark.parametrize("case", ["mfma_uniform", "mfma_balanced_paged", "valu_olse"])
+def test_fused_never_reads_stale_states(case):
+    """The last workgroup of a group must read the states its group published
+    in this call, never what the workspace held before. The workspace is first
+    filled with states that would dominate any merge they entered (max 1e4,
+    vectors 1e6), then left holding a previous call's states on other inputs;
+    each fused call must still match the oracle."""
+    if case == "mfma_uniform":
+        mk = lambda i, lens: W.contiguous(f"stale_{case}_{i}", seed=400 + i, batch=2, q_heads=64, kv_heads=8,
+                                          head_dim=128, capacity=12000, seq_lens=lens, dtype="f16")
+        lens_seq, opts = ([12000, 9000], [7001, 12000], [12000, 12000]), {"force_splits": 32}
+    elif case == "mfma_balanced_paged":
+        mk = lambda i, lens: W.paged(f"stale_{case}_{i}", seed=410 + i, batch=5, q_heads=32, kv_heads=8,
+                                     head_dim=128, seq_lens=lens, page_size=16, dtype="bf16")
+        lens_seq = ([9000, 40, 3000, 0, 7000], [8000, 2999, 6000, 700, 1], [9000, 9000, 9000, 9000, 9000])
+        opts = {"schedule": "balanced"}
+    else:
+        mk = lambda i, lens: W.contiguous(f"stale_{case}_{i}", seed=420 + i, batch=3, q_heads=8, kv_heads=8,
+                                          head_dim=128, capacity=6000, seq_lens=lens, dtype="bf16")
+        lens_seq, opts = ([6000, 5, 3000], [4000, 6000, 1]), {"force_splits": 12, "ws_format": "olse"}
+    dev = torch.device("cuda", 0)
+    ws = None
+    for i, lens in enumerate(lens_seq):
+        w = mk(i, lens)
+        q, k, v, sl = w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_lens.to(dev)
+        bt = None if w.block_table is None else w.block_table.to(dev)
+        o = dict(opts)
+        if o.get("schedule") == "balanced":
+            o["host_seq_lens"] = lens
+        plan = fd.fd_plan(fd.problem_for(q, k, v, sl, bt, max_seq_len=w.max_seq_len), **o)
+        if ws is None:                               # sized for the largest plan of the sequence
+            big = max(plan.ws_o_bytes, 1 << 22) // 4 * 2
+            ws = (torch.full((big,), 1e6, device=dev), torch.full((big // 64,), 1e4, device=dev),
+                  torch.zeros(4096, dtype=torch.int32, device=dev))
+        ws_o, ws_stats, ctr = ws
+        assert ws_o.numel() * 4 >= plan.ws_o_bytes and ws_stats.numel() * 4 >= plan.ws_stats_bytes
+        out = torch.empty(*q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=dev)
+        H.say(f"stale {case} call {i}: S={plan.num_splits} schedule={plan.schedule}")
+        fd.fd_decode_fused(plan, q, k, v, sl, ws_o, ws_stats, ctr, out, lse, bt)
+        torch.cuda.synchronize()
+        assert torch.all(ctr == 0).item()
+        H.check_against_oracle(w, out.cpu(), lse.cpu())
+
+
 def test_fused_agrees_with_two_launch_path():
     w = W.contiguous("fused_vs_split", seed=86, batch=1, q_heads=64, kv_heads=8, head_dim=128, capacity=20000,
                      seq_lens=[20000], dtype="f16")
