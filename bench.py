@@ -10,9 +10,10 @@ twice the 256 MB Infinity Cache, so no step is served from the previous one.
 
 Prints ONE JSON line: value = achieved K/V bandwidth in TB/s (algorithmic
 K+V bytes of the step / wall time per step), the microseconds per layer-step,
-a roofline object for the split kernel (its average duration from HIP events
-recorded on the launch stream) and the float64 CPU oracle timed on the host
-over a bounded sample of the same workload.
+a roofline object for the split kernel (its average duration from two HIP
+events on the launch stream around back-to-back launches of that kernel
+alone) and the float64 CPU oracle timed on the host over a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -96,6 +97,7 @@ def kernel_source_hash(kernel: str = "mfma") -> str:
     h = hashlib.sha256()
     for rel in (f"decode_attention_fd_amd/csrc/split_{kernel}.hip", "decode_attention_fd_amd/csrc/balance.h",
                 "decode_attention_fd_amd/csrc/merge_rows.h", "decode_attention_fd_amd/csrc/fd_internal.h",
+                "decode_attention_fd_amd/csrc/geometry.h",
                 "include/fd.h"):
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(rel.encode() + fh.read())
@@ -189,10 +191,13 @@ def cpu_baseline(w, max_heads: int):
     sampled_fraction = sum(per_head_bytes) / (sum(lens) * cache.Hq * 2 * cache.D * cpu.k.element_size())
     step_s = dt / max(sampled_fraction, 1e-12)
     kv_bytes = w.kv_bytes()
+    # host CPUs this process may run on, and the threads the oracle's NumPy/BLAS
+    # calls actually use (capped by the environment's thread limits)
+    cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [torch.get_num_threads()])
     return {
-        "value": kv_bytes / step_s / 1e12, "unit": "TB/s", "us_per_step": step_s * 1e6, "cores": threads,
-        "kind": "oracle",
+        "value": kv_bytes / step_s / 1e12, "unit": "TB/s", "us_per_step": step_s * 1e6,
+        "cores": min(cpus, threads), "host_cpus": cpus, "os_cpu_count": os.cpu_count(), "kind": "oracle",
         "sample": f"{len(pairs)} of {cache.B * cache.Hq} (sequence, query head) outputs of copy 0 in float64, "
                   f"{len(passes)} passes in {sum(passes):.1f} s (median pass {dt:.2f} s), scaled by their share of "
                   f"the step's KV bytes ({sampled_fraction:.3f})",
@@ -300,15 +305,39 @@ def main():
     wall = time.perf_counter() - t0
     us_step = wall / args.steps * 1e6
 
-    # per-kernel durations: same steps again with events on the launch stream
+    # Per-kernel durations, each kernel alone: two events on the launch stream
+    # bracket K back-to-back launches (rotating the same K/V copies), so the
+    # average is the kernel's own duration without per-launch event overhead
+    # (the basis of roofline.achieved; it is what a rocprofv3 kernel trace of
+    # the same command averages).
+    def bracket(launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(min(args.warmup, 5)):
+            launch(i)
+        e0.record(stream)
+        for i in range(args.steps):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    def split_only(i):
+        w = ws[i % copies]
+        if path == "fused":
+            fd.fd_decode_fused(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, ctr, out, lse, w.block_table, stream)
+        else:
+            fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
+
+    split_us = bracket(split_only)
+    merge_us = 0.0 if path == "fused" else bracket(lambda i: fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream))
+
+    # the step's distribution and per-launch event durations (events between the
+    # kernels of every step; these include the events' own overhead)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    split_us = sum(split_ms) / len(split_ms) * 1e3
-    merge_us = sum(merge_ms) / len(merge_ms) * 1e3
+    split_ev_us = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e3
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
 
     def pct(xs, q):
@@ -384,12 +413,15 @@ def main():
         "step_event_us": {"p10": pct(step_ms, 0.1), "p50": pct(step_ms, 0.5), "p90": pct(step_ms, 0.9)},
         "split_kernel_us": round(split_us, 2),
         "merge_kernel_us": round(merge_us, 2),
+        "split_kernel_event_us": round(split_ev_us, 2),
         "merge_share": round(merge_us / max(split_us + merge_us, 1e-9), 4),
         "bytes_per_step": moved,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": "split", "bytes_per_launch": step_kv, "kernel_source_hash": khash,
+            "kernel": "fused split" if path == "fused" else "split", "bytes_per_launch": step_kv,
+            "kernel_source_hash": khash,
+            "basis": f"HIP events on the launch stream around {args.steps} back-to-back launches of the kernel alone",
         },
         "read_probe": {"value": round(probe_gbps, 1), "unit": "GB/s", "bytes": probe_bytes,
                        "us": round(probe_us, 2), "split_kernel_frac_of_probe": round(achieved / probe_gbps, 4)},
