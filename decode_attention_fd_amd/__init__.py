@@ -108,6 +108,9 @@ def lib() -> ctypes.CDLL:
         L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge.restype = ctypes.c_int
+        L.fd_decode_fused_noalloc.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        L.fd_decode_fused_noalloc.restype = ctypes.c_int
         L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.fd_merge_states.restype = ctypes.c_int
@@ -339,6 +342,22 @@ def fd_decode_fused(plan: Plan, q, k, v, seq_lens, ws_o, ws_stats, ctr, out, lse
                                _ptr(ws_stats), ws_stats.numel() * ws_stats.element_size(), _ptr(ctr),
                                ctr.numel() * ctr.element_size(), _ptr(out), _ptr(lse), _stream_handle(stream))
     _check(st, "fd_decode_fused")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fd_decode_fused_noalloc(plan: Plan, q, k, v, seq_lens, out, lse=None, block_table=None, stream=None) -> None:
+    """fd_decode_fused with the library's static device scratch as workspace and
+    counters: nothing is allocated (for graph capture and allocation-free loops).
+    Calls on one GPU share that scratch and must not overlap in time."""
+    _check_inputs(plan, q, k, v, seq_lens, block_table)
+    _check_outputs(plan, out, lse)
+    _device_of([q, out, lse])
+    a = Args(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_table))
+    st = lib().fd_decode_fused_noalloc(ctypes.byref(plan), ctypes.byref(a), _ptr(out), _ptr(lse),
+                                       _stream_handle(stream))
+    _check(st, "fd_decode_fused_noalloc")
 
 
 def fd_merge(plan: Plan, ws_o, ws_stats, out, lse=None, stream=None) -> None:

@@ -274,6 +274,20 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
                            float* ws_stats, size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes,
                            float* out, float* lse, void* stream) {
   SplitParams p;
+  int st = fd::fused_params(plan, args, ws_o, ws_o_bytes, ws_stats, ws_stats_bytes, counters, counters_bytes, out,
+                            lse, &p);
+  if (st != FD_OK) return st;
+  return fd::launch_fused(plan, p, stream);
+}
+
+}  // extern "C"
+
+// The validation and launch of fd_decode_fused, shared with
+// fd_decode_fused_noalloc (noalloc.hip).
+int fd::fused_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes, float* ws_stats,
+                     size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes, float* out, float* lse,
+                     SplitParams* out_params) {
+  SplitParams& p = *out_params;
   int st = split_params(plan, args, ws_o, ws_o_bytes, ws_stats, ws_stats_bytes, &p);
   if (st != FD_OK) return st;
   if (!counters || !out) return FD_ERR_INVALID_ARG;
@@ -283,8 +297,16 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
   p.counters = counters;
   p.out = out;
   p.lse = lse;
-  return launch_split(plan, p, stream);
+  return FD_OK;
 }
+
+int fd::launch_fused(const fd_plan_t* plan, const SplitParams& p, void* stream) { return launch_split(plan, p, stream); }
+
+int fd::check_fused_plan(const fd_plan_t* plan) { return check_plan(plan); }
+
+int fd::record_hip_error(int err, const char* where) { return hip_fail(err, where); }
+
+extern "C" {
 
 FD_API int fd_merge(const fd_plan_t* plan, const float* ws_o, size_t ws_o_bytes, const float* ws_stats,
                     size_t ws_stats_bytes, float* out, float* lse, void* stream) {

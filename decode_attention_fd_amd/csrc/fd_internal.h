@@ -73,6 +73,16 @@ int validate_problem(const fd_problem* prob);
 int choose_kernel(const fd_problem* prob, int requested);
 uint64_t plan_checksum(const fd_plan_t* plan);
 
+// fd_decode_fused in two steps (api.cpp): every check and the launch
+// parameters, then the launch. The no-allocation entry point (noalloc.hip)
+// runs both with its static scratch as workspace and counters.
+int fused_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t ws_o_bytes, float* ws_stats,
+                 size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes, float* out, float* lse,
+                 SplitParams* p);
+int launch_fused(const fd_plan_t* plan, const SplitParams& p, void* stream);
+int check_fused_plan(const fd_plan_t* plan);       // FD_OK or the status fd_decode_fused would return
+int record_hip_error(int err, const char* where);  // keeps the text for fd_last_hip_error; FD_ERR_HIP
+
 // Element size of an fd_dtype, 0 if invalid.
 inline int dtype_size(int dt) {
   return dt == FD_DTYPE_F32 ? 4 : (dt == FD_DTYPE_F16 || dt == FD_DTYPE_BF16) ? 2 : 0;

@@ -289,6 +289,22 @@ FD_API int fd_decode_fused(const fd_plan_t* plan, const fd_args* args, float* ws
                            float* ws_stats, size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes,
                            float* out, float* lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as fd_decode_fused, with the workspace and the arrival counters in a
+ * static device array of FD_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends, so the caller passes only the
+ * inputs and outputs. Each call first clears the counters with a small fill
+ * kernel, then launches the fused kernel, both on `stream`. Needs
+ * align256(ws_counter_bytes) + align256(ws_o_bytes) + ws_stats_bytes of the
+ * plan to be at most FD_NOALLOC_SCRATCH_BYTES, else FD_ERR_WORKSPACE (nothing
+ * is launched). Every call on one GPU shares that GPU's array and leaves its
+ * last contents there: calls that overlap in time on one GPU race, so issue
+ * them on one stream. Allocates nothing (no hipMalloc, no allocating library
+ * call); the first call on a device looks up that device's array address. */
+#define FD_NOALLOC_SCRATCH_BYTES (32 << 20)
+FD_API int fd_decode_fused_noalloc(const fd_plan_t* plan, const fd_args* args, float* out, float* lse, void* stream);
+
 /* Merge externally produced attention states, one output per row: the ⊕
  * operator of kanthi.in §2 (stable form) exposed on its own, for cascade
  * attention over shared prefixes and for states gathered from other devices

@@ -425,6 +425,34 @@ def test_binding_checks_tensors_against_the_plan():
     assert "ws_o" in msg(lambda: fd.fd_merge(plan, ws_o.double(), ws_st, out, lse))
 
 
+def test_noalloc_validation_without_gpu():
+    """fd_decode_fused_noalloc checks everything on the host before any HIP
+    call: a plan whose workspace and counters exceed the static scratch, a
+    tampered plan, missing arguments and misaligned outputs."""
+    L = fd.lib()
+    hdr = open(HEADER).read()
+    m = re.search(r"#define FD_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == fd.NOALLOC_SCRATCH_BYTES
+    good = fd.Args(0x10000, 0x20000, 0x30000, 0x40000, None)
+    plan = fd.fd_plan(contiguous_problem(B=2, Hq=64, Hkv=8, L=20000), num_cus=256)
+
+    def call(pl, args=good, out=0x50000, lse=None):
+        return L.fd_decode_fused_noalloc(ctypes.byref(pl), ctypes.byref(args) if args is not None else None,
+                                         out, lse, None)
+
+    assert call(plan, args=None) == fd.FD_ERR_INVALID_ARG
+    assert call(plan, out=None) == fd.FD_ERR_INVALID_ARG
+    assert call(plan, out=0x50004) == fd.FD_ERR_ALIGNMENT
+    assert call(plan, args=fd.Args(0x10008, 0x20000, 0x30000, 0x40000, None)) == fd.FD_ERR_ALIGNMENT
+    bad = fd.Plan.from_buffer_copy(plan)
+    bad.num_splits += 1
+    assert call(bad) == fd.FD_ERR_BAD_PLAN
+    # 256 sequences x 64 query heads x 128 splits of fp32 states: 32 MiB of ws_o alone
+    big = fd.fd_plan(contiguous_problem(B=256, Hq=64, Hkv=8, L=100000), num_cus=256, force_splits=128)
+    assert big.ws_o_bytes >= fd.NOALLOC_SCRATCH_BYTES
+    assert call(big) == fd.FD_ERR_WORKSPACE
+
+
 def test_merge_states_validation_without_gpu():
     """Every argument error of fd_merge_states is caught on the host, before
     any launch (so none of these calls touches a device)."""
