@@ -134,9 +134,10 @@ def _pmc_rows(d: str, counter: str):
     return rows
 
 
-def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> None:
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str, out_path: str = "") -> None:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, scaled by the
-    same counters on the calibration copy (COPY_BYTES read and written)."""
+    same counters on the calibration copy (COPY_BYTES read and written). Writes
+    profiles/traffic_split_<workload>.json (or out_path; "-": print only)."""
     names = [n for n, _ in _pmc_rows(fetch_dir, "FETCH_SIZE") if "split_" in n and "kernel" in n]
     kernel = "valu" if names and all("split_valu" in n for n in names) else "mfma"
     out = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
@@ -154,10 +155,37 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> None:
                     "copy_kib_per_dispatch": copy_kib, "scale": factor,
                     "bytes_per_launch": split_kib * 1024.0 * factor}
     out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
-    path = os.path.join(ROOT, "profiles", f"traffic_split_{workload}.json")
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
+    path = out_path or os.path.join(ROOT, "profiles", f"traffic_split_{workload}.json")
+    if path != "-":
+        with open(path, "w") as f:
+            json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def pmc_dump(dirs) -> None:
+    """Average of every counter per kernel over the dispatches in rocprofv3
+    --pmc CSV directories (one JSON line per directory and kernel), and the
+    average duration per kernel from --kernel-trace directories."""
+    import csv
+    import glob
+
+    for d in dirs:
+        acc = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = (r["Kernel_Name"], r["Counter_Name"])
+                    acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    acc[(r["Name"], "average_ns")] = [float(r["AverageNs"])]
+                    acc[(r["Name"], "calls")] = [float(r["Calls"])]
+        kernels = sorted({k for k, _ in acc})
+        for kern in kernels:
+            row = {c: sum(v) / len(v) for (k, c), v in acc.items() if k == kern}
+            row["dispatches"] = max(len(v) for (k, c), v in acc.items() if k == kern)
+            print(json.dumps({"dir": d, "kernel": kern[:120], **row}))
 
 
 def cpu_baseline(w, max_heads: int):
@@ -204,6 +232,107 @@ def cpu_baseline(w, max_heads: int):
     }, out, pairs
 
 
+SWEEP_BATCHES = (1, 4, 16, 64)
+SWEEP_CONTEXTS = (1024, 4096, 16384, 65536, 131072)
+SWEEP_MAX_TOKENS = 1 << 20          # B x L per point (4 GiB of fp16 K/V at 8 KV heads, D = 128)
+
+
+def sweep_speedup(q_heads: int = 64, kv_heads: int = 8, min_ms: float = 20.0) -> None:
+    """Speedup of split-KV decode over one split per (sequence, KV head), the
+    performance check of the kanthi.in chapter's section 8 ("speedup vs
+    num_splits = 1 across a (batch, context) sweep"): for every (B, L) with
+    B x L <= SWEEP_MAX_TOKENS, GQA q_heads/kv_heads, D = 128, fp16, equal
+    lengths L, the step of the planner's plan (split + merge, or the fused call
+    where bench.choose_path takes it) against force_splits = 1 (the fused call,
+    which then writes its rows directly, one launch). K/V copies rotate so
+    that together they exceed twice the 256 MB Infinity Cache; each plan is
+    timed by wall clock over enough steps for min_ms (eager launches through
+    the binding: small steps then measure the host's launch rate) and by
+    events around the replay of a HIP graph holding the same steps (device
+    time alone; the graph has no memset node, the fused counters return to
+    zero inside the kernels). One JSON line per point."""
+    import torch
+
+    import decode_attention_fd_amd as fd
+    import fd_workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    for B in SWEEP_BATCHES:
+        for L in SWEEP_CONTEXTS:
+            if B * L > SWEEP_MAX_TOKENS:
+                continue
+            w0 = W.contiguous(f"sweep_B{B}_L{L}", seed=B * 1000003 + L, batch=B, q_heads=q_heads, kv_heads=kv_heads,
+                              head_dim=128, capacity=L, seq_lens=[L] * B, dtype="f16", device=dev)
+            kv = w0.kv_bytes()
+            copies = min(128, max(2, math.ceil(2 * MALL_BYTES / kv) + 1))
+            ws = [w0] + [W.redraw_kv(w0, 9000 + i) for i in range(1, copies)]
+            prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, max_seq_len=L)
+            row = {"batch": B, "context": L, "q_heads": q_heads, "kv_heads": kv_heads, "kv_bytes": kv,
+                   "kv_copies": copies}
+            for tag, opts in (("plan", {"host_seq_lens": [L] * B}), ("one_split", {"force_splits": 1})):
+                plan = fd.fd_plan(prob, **opts)
+                path = choose_path(plan) if tag == "plan" else "fused"
+                ws_o, ws_stats = fd.workspace(plan, dev)
+                ctr = fd.counters(plan, dev)
+                out = torch.empty(B, q_heads, 128, dtype=torch.float32, device=dev)
+                lse = torch.empty(B, q_heads, dtype=torch.float32, device=dev)
+
+                def step(i):
+                    w = ws[i % copies]
+                    if path == "fused":
+                        fd.fd_decode_fused(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, ctr, out, lse, None,
+                                           stream)
+                    else:
+                        fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, None, stream)
+                        fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+
+                for i in range(3):
+                    step(i)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                step(0)
+                torch.cuda.synchronize()
+                once = time.perf_counter() - t0
+                n = int(min(400, max(5, min_ms * 1e-3 / max(once, 1e-6))))
+                t0 = time.perf_counter()
+                for i in range(n):
+                    step(i)
+                torch.cuda.synchronize()
+                us = (time.perf_counter() - t0) / n * 1e6
+                # the same steps from a HIP graph
+                ng = min(n, 64)
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(side):
+                    with torch.cuda.graph(graph, stream=side):
+                        stream = torch.cuda.current_stream()
+                        for i in range(ng):
+                            step(i)
+                stream = torch.cuda.current_stream()
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = max(1, n // ng)
+                e0.record(stream)
+                for _ in range(reps):
+                    graph.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                gus = e0.elapsed_time(e1) * 1e3 / (reps * ng)
+                del graph
+                row[tag] = {"us": round(us, 2), "tbps": round(kv / (us * 1e-6) / 1e12, 3), "graph_us": round(gus, 2),
+                            "graph_tbps": round(kv / (gus * 1e-6) / 1e12, 3), "num_splits": plan.num_splits,
+                            "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "path": path, "steps": n}
+            row["speedup"] = round(row["one_split"]["us"] / row["plan"]["us"], 2)
+            row["graph_speedup"] = round(row["one_split"]["graph_us"] / row["plan"]["graph_us"], 2)
+            print(json.dumps(row), flush=True)
+            del ws, w0
+
+
 def build_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +354,15 @@ def build_parser() -> argparse.ArgumentParser:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
+    ap.add_argument("--sweep-speedup", action="store_true",
+                    help="time the planner's plan against one split per (sequence, KV head) over a (batch, context) "
+                         "sweep of 64/8 GQA fp16 steps; one JSON line per point, then exit")
+    ap.add_argument("--pmc-dump", nargs="+", metavar="DIR",
+                    help="print per-kernel counter averages (and kernel-trace durations) of rocprofv3 CSV "
+                         "directories, one JSON line per directory and kernel, and exit")
+    ap.add_argument("--pmc-out", default="",
+                    help="--pmc-summary: where to write the record (default profiles/traffic_split_<workload>.json; "
+                         "'-': print only)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench into "
                          "profiles/traffic_split_<workload>.json and exit")
@@ -233,14 +371,20 @@ def build_parser() -> argparse.ArgumentParser:
 
 def main():
     args = build_parser().parse_args()
+    if args.pmc_dump:
+        pmc_dump(args.pmc_dump)
+        return
     if args.pmc_summary:
-        pmc_summary(args.workload, *args.pmc_summary)
+        pmc_summary(args.workload, *args.pmc_summary, out_path=args.pmc_out)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs the decode on a single device "
               "(sharding across GPUs is a design note, not built); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep_speedup:
+        sweep_speedup()
+        return
 
     import torch
 
@@ -329,15 +473,17 @@ def main():
             fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
 
     split_us = bracket(split_only)
-    merge_us = 0.0 if path == "fused" else bracket(lambda i: fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream))
 
     # the step's distribution and per-launch event durations (events between the
-    # kernels of every step; these include the events' own overhead)
+    # kernels of every step; these include the events' own overhead). The merge
+    # kernel is timed this way: a few microseconds long, back-to-back launches
+    # of it would measure the host's launch rate instead.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     split_ev_us = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e3
+    merge_us = 0.0 if path == "fused" else sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs) * 1e3
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
 
     def pct(xs, q):
@@ -412,7 +558,7 @@ def main():
         },
         "step_event_us": {"p10": pct(step_ms, 0.1), "p50": pct(step_ms, 0.5), "p90": pct(step_ms, 0.9)},
         "split_kernel_us": round(split_us, 2),
-        "merge_kernel_us": round(merge_us, 2),
+        "merge_kernel_event_us": round(merge_us, 2),
         "split_kernel_event_us": round(split_ev_us, 2),
         "merge_share": round(merge_us / max(split_us + merge_us, 1e-9), 4),
         "bytes_per_step": moved,

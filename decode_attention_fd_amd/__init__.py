@@ -21,7 +21,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfd.so")
+# FD_LIB_PATH names another build of the library (a measurement variant built
+# with decode_attention_fd_amd/build.py --waves N --out PATH).
+LIB_PATH = os.environ.get("FD_LIB_PATH") or os.path.join(_HERE, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_ALIGNMENT, FD_ERR_WORKSPACE, FD_ERR_HIP, FD_ERR_BAD_PLAN = range(7)
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -93,43 +95,50 @@ def lib() -> ctypes.CDLL:
     """The loaded ``libfd.so``; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_fd_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        L.fd_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), ctypes.POINTER(Plan)]
-        L.fd_plan.restype = ctypes.c_int
-        L.fd_decode_split.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
-                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        L.fd_decode_split.restype = ctypes.c_int
-        L.fd_decode_fused.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
-                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.fd_decode_fused.restype = ctypes.c_int
-        L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                               ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.fd_merge.restype = ctypes.c_int
-        L.fd_decode_fused_noalloc.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
-                                              ctypes.c_void_p, ctypes.c_void_p]
-        L.fd_decode_fused_noalloc.restype = ctypes.c_int
-        L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.fd_merge_states.restype = ctypes.c_int
-        L.fd_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                    ctypes.c_void_p]
-        L.fd_read_probe.restype = ctypes.c_int
-        L.fd_status_str.argtypes = [ctypes.c_int]
-        L.fd_status_str.restype = ctypes.c_char_p
-        L.fd_last_hip_error.argtypes = []
-        L.fd_last_hip_error.restype = ctypes.c_char_p
-        L.fd_version.argtypes = []
-        L.fd_version.restype = ctypes.c_char_p
-        L.fd_struct_size.argtypes = [ctypes.c_int]
-        L.fd_struct_size.restype = ctypes.c_size_t
-        for i, cls in enumerate((Problem, PlanOpts, Plan, Args)):
-            if L.fd_struct_size(i) != ctypes.sizeof(cls):
-                raise RuntimeError(f"ABI mismatch for {cls.__name__}: C {L.fd_struct_size(i)} vs {ctypes.sizeof(cls)}")
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Open a build of the library at ``path`` with the C signatures set (the
+    race-check build is opened beside libfd.so this way); raises if missing or
+    if its struct layouts differ from this binding's."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m decode_attention_fd_amd.build`")
+    L = ctypes.CDLL(path)
+    L.fd_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(PlanOpts), ctypes.POINTER(Plan)]
+    L.fd_plan.restype = ctypes.c_int
+    L.fd_decode_split.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.fd_decode_split.restype = ctypes.c_int
+    L.fd_decode_fused.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.fd_decode_fused.restype = ctypes.c_int
+    L.fd_merge.argtypes = [ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                           ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.fd_merge.restype = ctypes.c_int
+    L.fd_decode_fused_noalloc.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    L.fd_decode_fused_noalloc.restype = ctypes.c_int
+    L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.fd_merge_states.restype = ctypes.c_int
+    L.fd_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p]
+    L.fd_read_probe.restype = ctypes.c_int
+    L.fd_status_str.argtypes = [ctypes.c_int]
+    L.fd_status_str.restype = ctypes.c_char_p
+    L.fd_last_hip_error.argtypes = []
+    L.fd_last_hip_error.restype = ctypes.c_char_p
+    L.fd_version.argtypes = []
+    L.fd_version.restype = ctypes.c_char_p
+    L.fd_struct_size.argtypes = [ctypes.c_int]
+    L.fd_struct_size.restype = ctypes.c_size_t
+    for i, cls in enumerate((Problem, PlanOpts, Plan, Args)):
+        if L.fd_struct_size(i) != ctypes.sizeof(cls):
+            raise RuntimeError(f"ABI mismatch for {cls.__name__}: C {L.fd_struct_size(i)} vs {ctypes.sizeof(cls)}")
+    return L
 
 
 def status_str(status: int) -> str:

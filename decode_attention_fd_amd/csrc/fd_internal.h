@@ -6,6 +6,28 @@
 
 #include "fd.h"
 
+// Race check: a build with FD_DEBUG_BARRIERS defined (build.py
+// --debug-barriers) adds synchronisation around every hand-over of LDS, and
+// its results must equal the release build's bit for bit. Workgroup barriers
+// go only where every thread of the workgroup arrives; inside the per-wave
+// streaming loops, whose trip counts differ between waves, the debug build
+// waits for all of the wave's memory operations and adds a wave barrier.
+#ifdef FD_DEBUG_BARRIERS
+#define FD_DEBUG_WG_BARRIER() __syncthreads()
+#define FD_DEBUG_WAVE_BARRIER()         \
+  do {                                  \
+    __builtin_amdgcn_s_waitcnt(0);      \
+    __builtin_amdgcn_wave_barrier();    \
+  } while (0)
+#else
+#define FD_DEBUG_WG_BARRIER() \
+  do {                        \
+  } while (0)
+#define FD_DEBUG_WAVE_BARRIER() \
+  do {                          \
+  } while (0)
+#endif
+
 namespace fd {
 
 // Everything one split-kernel launch needs, passed by value. Strides are in

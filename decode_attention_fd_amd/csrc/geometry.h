@@ -4,9 +4,16 @@
 // the kernels stream.
 #pragma once
 
+// Waves per split workgroup, both kernels: 4 unless the build sets another
+// value (decode_attention_fd_amd/build.py --waves; for measurements).
+#ifndef FD_SPLIT_WAVES
+#define FD_SPLIT_WAVES 4
+#endif
+
 namespace fd {
 
-constexpr int kSplitWaves = 4;           // waves per split workgroup, both kernels
+constexpr int kSplitWaves = FD_SPLIT_WAVES;   // waves per split workgroup, both kernels
+static_assert(kSplitWaves >= 1 && kSplitWaves <= 16, "1 to 16 waves per split workgroup");
 constexpr int kMfmaTileTokens = 32;      // KV tokens per wave tile, MFMA kernel
 constexpr int kValuLoadsPerTile = 8;     // 16-byte load instructions per wave tile per tensor, VALU kernel
 

@@ -119,6 +119,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
   using G = Geo<D>;
   using V8 = typename Mma<T>::vec;
   using VR = typename VRead<G::VW>::type;
+  FD_DEBUG_WG_BARRIER();                // every thread calls split_piece
   auto& lds = sm.lds;
   auto& st_m = sm.st_m;
   auto& st_l = sm.st_l;
@@ -338,14 +339,18 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       store(vr, ldsV);
       issue(vr, vbase, tstart(tile + NW), pid_next);
       if (PAGED) pid_next = pid_after;
+      FD_DEBUG_WAVE_BARRIER();          // the tile stored, before the wave reads it
       compute(start + tile * TT);
+      FD_DEBUG_WAVE_BARRIER();          // the tile read, before the next one overwrites it
     }
     if (my_tiles > 0) {                                     // the wave's last tile: nothing more to request
       store(kr, ldsK);
       store(vr, ldsV);
+      FD_DEBUG_WAVE_BARRIER();
       compute(start + tile * TT);
     }
   }
+  FD_DEBUG_WAVE_BARRIER();              // the last tile read, before the state overwrites the slice
 
   // ---- per-wave state -> LDS: tile ct in lds[wave][ct] as ow[column][d],
   // d = NDB*(4*grp + i) + e; statistics at st_m/st_l[wave][16*ct + column]
@@ -432,6 +437,7 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
       }
     }
   }
+  FD_DEBUG_WG_BARRIER();                // the states read from LDS, before any later reuse
 }
 
 // Uniform schedule: workgroup (s, kvh, b) owns split s of segment (b, kvh).

@@ -308,6 +308,7 @@ __device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>&
   };
   for (int it = 0; it + 1 < my_tiles; ++it, tile += NW) step(tile, true);
   if (my_tiles > 0) step(tile, false);
+  FD_DEBUG_WG_BARRIER();                // every wave done with the stream, before the states go to LDS
 
   // ---- row-group states -> LDS, then one exact merge per (head, dim)
 #pragma unroll
@@ -360,6 +361,7 @@ __device__ __forceinline__ void valu_piece(const SplitParams& p, VSmem<D, T, G>&
       if (d == 0) ws_store(p.ws_stats + base, empty ? -INFINITY : (M + log2f(L)) * LN2, co);
     }
   }
+  FD_DEBUG_WG_BARRIER();                // the states read from LDS, before any later reuse
 }
 
 // Uniform schedule: workgroup (s, kvh, b) owns split s of segment (b, kvh).
