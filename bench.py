@@ -58,7 +58,7 @@ def make_workload(name: str, device):
 
 
 def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0, kernel: str = "auto",
-                 piece_cost: int = 0) -> dict:
+                 piece_cost: int = 0, odd_xcd_permille: int = 0) -> dict:
     """fd_plan options of a benchmark run: the workload's forced splits or
     chunk if it has them, else the planner fed the host copy of the lengths."""
     opts = {"ws_format": w.ws_format}
@@ -77,6 +77,8 @@ def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0
         opts["kernel"] = kernel
     if piece_cost:
         opts["piece_cost_tokens"] = piece_cost
+    if odd_xcd_permille:
+        opts["odd_xcd_permille"] = odd_xcd_permille
     return opts
 
 
@@ -186,6 +188,76 @@ def pmc_dump(dirs) -> None:
             row = {c: sum(v) / len(v) for (k, c), v in acc.items() if k == kern}
             row["dispatches"] = max(len(v) for (k, c), v in acc.items() if k == kern)
             print(json.dumps({"dir": d, "kernel": kern[:120], **row}))
+
+
+def wg_stamp_report(plan, launch, launches: int, torch, fd, stream) -> dict:
+    """Per-workgroup stamps of `launches` launches of the split kernel (the
+    per-workgroup stamp build, loaded through FD_LIB_PATH): each workgroup's
+    end and duration relative to the launch's first start, its tokens, pieces
+    and XCD, summarised by piece count and by XCD."""
+    import numpy as np
+
+    nwg = plan.grid_x * plan.grid_y * plan.grid_z
+    buf = torch.zeros(fd.WG_STAMP_RECORDS * 4, dtype=torch.int64, device=stream.device)
+    recs = []
+    for i in range(launches):
+        launch(i)
+        st = fd.lib().fd_wg_stamps(ctypes_void_p(buf.data_ptr()), buf.numel() * 8, ctypes_void_p(stream.cuda_stream))
+        if st != 0:
+            raise SystemExit(f"fd_wg_stamps: {fd.status_str(st)} (run with FD_LIB_PATH naming the --wg-stamps build)")
+        torch.cuda.synchronize()
+        r = buf[:4 * nwg].view(nwg, 4).cpu().numpy().astype(np.int64)
+        t0 = r[:, 0].min()
+        recs.append(np.stack([r[:, 0] - t0, r[:, 1] - t0, r[:, 2], r[:, 3] & 0xFFFFFFFF, r[:, 3] >> 32], 1))
+    a = np.stack(recs)                                 # [launch, wg, (start, end, tokens, pieces, xcc)] in 10 ns ticks
+    start_us, end_us = a[..., 0] / 100.0, a[..., 1] / 100.0
+    dur_us = end_us - start_us
+    tokens, pieces, xcc = a[..., 2], a[..., 3], a[..., 4]
+    q = lambda x: [round(float(v), 2) for v in np.percentile(x, [0, 10, 50, 90, 100])]
+    out = {"workgroups": int(nwg), "launches": int(launches),
+           "end_us_min_p10_p50_p90_max": q(end_us), "duration_us_min_p10_p50_p90_max": q(dur_us),
+           "start_us_max": round(float(start_us.max()), 2),
+           "tokens_per_wg_min_p50_max": [int(tokens.min()), int(np.median(tokens)), int(tokens.max())]}
+    byp = {}
+    for n in sorted(set(pieces.ravel().tolist())):
+        m = pieces == n
+        byp[int(n)] = {"workgroups_per_launch": round(float(m.sum()) / launches, 1),
+                       "mean_end_us": round(float(end_us[m].mean()), 2),
+                       "mean_tokens": round(float(tokens[m].mean()), 1),
+                       "us_per_1k_tokens": round(float(dur_us[m].sum() / max(1, tokens[m].sum()) * 1e3), 3)}
+    out["by_pieces"] = byp
+    byx = {}
+    for x in sorted(set(xcc.ravel().tolist())):
+        m = xcc == x
+        byx[int(x)] = {"mean_end_us": round(float(end_us[m].mean()), 2), "max_end_us": round(float(end_us[m].max()), 2),
+                       "mean_tokens": round(float(tokens[m].mean()), 1)}
+    out["by_xcd"] = byx
+    # the launch's end against its busiest workgroups: a least-squares fit of duration on tokens and pieces
+    A = np.stack([tokens.ravel() / 1000.0, pieces.ravel(), np.ones(tokens.size)], 1)
+    coef, *_ = np.linalg.lstsq(A, dur_us.ravel(), rcond=None)
+    pred = A @ coef
+    resid = dur_us.ravel() - pred
+    out["fit_duration_us"] = {"per_1k_tokens": round(float(coef[0]), 3), "per_piece": round(float(coef[1]), 3),
+                              "constant": round(float(coef[2]), 3),
+                              "r2": round(float(1 - resid.var() / max(dur_us.var(), 1e-12)), 3)}
+    # per launch: how far the last workgroup ends past the mean end
+    spread = [float(end_us[i].max() - end_us[i].mean()) for i in range(launches)]
+    out["last_end_minus_mean_end_us"] = round(float(np.mean(spread)), 2)
+    # workgroups go to XCDs round-robin by linear index? and the odd / even XCDs' mean end per launch
+    lin = np.arange(nwg)
+    out["xcd_is_index_mod_8"] = round(float(np.mean(xcc == (lin % 8)[None, :])), 4)
+    odd = (xcc % 2) == 1
+    out["per_launch_mean_end_us_even_odd"] = [[round(float(end_us[i][~odd[i]].mean()), 2),
+                                               round(float(end_us[i][odd[i]].mean()), 2)] for i in range(launches)]
+    out["per_launch_max_end_us_even_odd"] = [[round(float(end_us[i][~odd[i]].max()), 2),
+                                              round(float(end_us[i][odd[i]].max()), 2)] for i in range(launches)]
+    return out
+
+
+def ctypes_void_p(x):
+    import ctypes
+
+    return ctypes.c_void_p(x)
 
 
 def cpu_baseline(w, max_heads: int):
@@ -351,12 +423,19 @@ def build_parser() -> argparse.ArgumentParser:
     ap.add_argument("--kernel", choices=["auto", "mfma", "valu"], default="auto", help="split kernel (auto: planner)")
     ap.add_argument("--piece-cost", type=int, default=0,
                     help="balanced schedule: start-up cost of one piece in KV tokens (0 = library default, -1 = none)")
+    ap.add_argument("--odd-xcd-permille", type=int, default=0,
+                    help="uniform plans: tokens shifted from odd-XCD to even-XCD splits, per mille "
+                         "(0 = library default, -1 = equal splits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy (known bytes) to scale PMC counters")
     ap.add_argument("--sweep-speedup", action="store_true",
                     help="time the planner's plan against one split per (sequence, KV head) over a (batch, context) "
                          "sweep of 64/8 GQA fp16 steps; one JSON line per point, then exit")
+    ap.add_argument("--wg-stamps", type=int, default=0, metavar="LAUNCHES",
+                    help="with FD_LIB_PATH naming the per-workgroup stamp build (build.py --wg-stamps): run the "
+                         "workload's split (or fused) kernel LAUNCHES times, print a summary of the workgroups' "
+                         "start/end stamps, tokens, pieces and XCDs as JSON, and exit")
     ap.add_argument("--pmc-dump", nargs="+", metavar="DIR",
                     help="print per-kernel counter averages (and kernel-trace durations) of rocprofv3 CSV "
                          "directories, one JSON line per directory and kernel, and exit")
@@ -403,7 +482,8 @@ def main():
     ws = [w0] + [W.redraw_kv(w0, 7000 + i) for i in range(1, copies)]
     torch.cuda.synchronize()
 
-    opts = plan_options(w0, args.splits, args.schedule, args.wgs_per_cu, args.kernel, args.piece_cost)
+    opts = plan_options(w0, args.splits, args.schedule, args.wgs_per_cu, args.kernel, args.piece_cost,
+                        args.odd_xcd_permille)
     prob = fd.problem_for(w0.q, w0.k, w0.v, w0.seq_lens, w0.block_table, max_seq_len=w0.max_seq_len)
     t0 = time.perf_counter()
     plan = fd.fd_plan(prob, **opts)
@@ -440,6 +520,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    if args.wg_stamps:
+        def launch(i):
+            w = ws[i % copies]
+            if path == "fused":
+                fd.fd_decode_fused(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, ctr, out, lse, w.block_table,
+                                   stream)
+            else:
+                fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
+
+        rep = wg_stamp_report(plan, launch, args.wg_stamps, torch, fd, stream)
+        rep.update({"workload": args.workload, "path": path, "num_splits": plan.num_splits,
+                    "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "lib": fd.LIB_PATH})
+        print(json.dumps(rep), flush=True)
+        return
 
     # timed region: exactly K steps, wall clock between synchronisations
     t0 = time.perf_counter()
@@ -552,6 +647,7 @@ def main():
             "head_dim": w0.head_dim, "max_seq_len": w0.max_seq_len, "kv_bytes_per_step": step_kv,
             "kv_bytes_allocated": alloc, "kv_copies": copies, "layout": "paged" if w0.paged else "contiguous",
             "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
+            "odd_chunk_tokens": plan.odd_chunk_tokens,
             "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
             "slots": plan.slots, "plan_us": round(plan_us, 1), "plan_first_us": round(plan_first_us, 1), "path": path,
             "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "grid": plan.grid_x * plan.grid_y * plan.grid_z,

@@ -56,7 +56,7 @@ class PlanOpts(ctypes.Structure):
         ("force_chunk_tokens", ctypes.c_int32), ("ws_format", ctypes.c_int32), ("kernel", ctypes.c_int32),
         ("heuristic", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("overhead_budget", ctypes.c_float),
         ("num_host_seq_lens", ctypes.c_int32), ("schedule", ctypes.c_int32), ("piece_cost_tokens", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("odd_xcd_permille", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
         ("host_seq_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
@@ -68,7 +68,7 @@ class Plan(ctypes.Structure):
         ("tile_tokens", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32), ("slots", ctypes.c_int32),
         ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
         ("scale", ctypes.c_float), ("schedule", ctypes.c_int32),
-        ("piece_cost", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+        ("piece_cost", ctypes.c_int32), ("odd_chunk_tokens", ctypes.c_int32),
         ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64), ("ws_counter_bytes", ctypes.c_int64),
         ("prob", Problem), ("checksum", ctypes.c_uint64),
     ]
@@ -124,6 +124,8 @@ def load(path: str) -> ctypes.CDLL:
     L.fd_merge_states.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.fd_merge_states.restype = ctypes.c_int
+    L.fd_wg_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.fd_wg_stamps.restype = ctypes.c_int
     L.fd_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]
     L.fd_read_probe.restype = ctypes.c_int
@@ -213,7 +215,8 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: tor
 def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_splits: int = 0,
             force_chunk_tokens: int = 0, ws_format: str = "uml", kernel: str = "auto",
             heuristic: str = "mi355x", max_splits: int = 0, overhead_budget: float = 0.0,
-            host_seq_lens=None, schedule: str = "auto", piece_cost_tokens: int = 0) -> Plan:
+            host_seq_lens=None, schedule: str = "auto", piece_cost_tokens: int = 0,
+            odd_xcd_permille: int = 0) -> Plan:
     """Call ``fd_plan``. ``num_cus=0`` asks the current device. ``host_seq_lens``
     (a host list / CPU tensor of the batch's lengths) enables length-aware
     splits and the balanced schedule."""
@@ -232,6 +235,7 @@ def fd_plan(problem: Problem, *, num_cus: int = 0, wgs_per_cu: int = 0, force_sp
     o.overhead_budget = overhead_budget
     o.schedule = SCHEDULES[schedule]
     o.piece_cost_tokens = piece_cost_tokens
+    o.odd_xcd_permille = odd_xcd_permille
     plan = Plan()
     _check(lib().fd_plan(ctypes.byref(problem), ctypes.byref(o), ctypes.byref(plan)), "fd_plan")
     del keep
@@ -413,6 +417,7 @@ def fd_merge_states(states, stats, out=None, lse_out=None, *, ws_format: str = "
 
 
 READ_PROBE_SINK_BYTES = 512 * 256 * 4
+WG_STAMP_RECORDS = 65536
 
 
 def fd_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -99,7 +99,7 @@ int check_plan(const fd_plan_t* plan) {
   if (!plan) return FD_ERR_INVALID_ARG;
   if (plan->magic != FD_PLAN_MAGIC || plan->checksum != plan_checksum(plan)) return FD_ERR_BAD_PLAN;
   if (validate_problem(&plan->prob) != FD_OK) return FD_ERR_BAD_PLAN;
-  if (plan->num_splits < 1 || plan->chunk_tokens < 1) return FD_ERR_BAD_PLAN;
+  if (plan->num_splits < 1 || plan->chunk_tokens < 1 || plan->odd_chunk_tokens < 1) return FD_ERR_BAD_PLAN;
   if (plan->schedule != FD_SCHEDULE_UNIFORM && plan->schedule != FD_SCHEDULE_BALANCED) return FD_ERR_BAD_PLAN;
   if (plan->schedule == FD_SCHEDULE_BALANCED && (plan->grid_x < 1 || plan->piece_cost < 0)) return FD_ERR_BAD_PLAN;
   return FD_OK;
@@ -228,6 +228,7 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
   p.R = p.g * p.q_len;
   p.S = plan->num_splits;
   p.chunk = plan->chunk_tokens;
+  p.chunk_odd = plan->odd_chunk_tokens;
   if (paged) {
     p.cap_tokens = pr.max_pages_per_seq * pr.page_size;
     p.page_log2 = ilog2(pr.page_size);
@@ -240,12 +241,14 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
     p.granule = plan->chunk_tokens;
     p.piece_cost = plan->piece_cost;
   } else {
-    // Tokens past S*chunk belong to no split: clamp there as well.
-    const int64_t covered = (int64_t)plan->num_splits * plan->chunk_tokens;
+    // Tokens past the last split belong to no split: clamp there as well.
+    const int64_t covered = (int64_t)(plan->num_splits / 2) * (plan->chunk_tokens + plan->odd_chunk_tokens) +
+                            (plan->num_splits % 2 ? plan->chunk_tokens : 0);
     if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
   }
   p.ws_format = plan->ws_format;
   p.scale_log2 = (float)((double)plan->scale * 1.4426950408889634);
+  p.stamps = wg_stamp_records_for((int64_t)plan->grid_x * plan->grid_y * plan->grid_z);
   return FD_OK;
 }
 

@@ -48,7 +48,8 @@ struct SplitParams {
   int32_t q_len;                        // query rows per sequence (>= 1)
   int64_t q_sq;                         // element stride between a sequence's query rows
   int32_t R;                            // state rows per (sequence, KV head): g * q_len
-  int32_t S, chunk;
+  int32_t S, chunk;                     // uniform: chunk = tokens of an even-numbered split
+  int32_t chunk_odd;                    // uniform: tokens of an odd-numbered split
   int32_t cap_tokens;                   // seq_lens are clamped to [0, cap_tokens]
   int32_t page_log2, num_pages;
   int32_t ws_format;
@@ -60,6 +61,7 @@ struct SplitParams {
   // fused merge (0 = write split states only)
   int32_t fused;
   uint32_t* counters;                   // [B * Hkv], zero on entry, zero on exit
+  uint64_t* stamps;                     // per-workgroup stamp records (measurement build), else null
   float* out;                           // [B, Hq, D]
   float* lse;                           // [B, Hq] or null
 };
@@ -102,6 +104,9 @@ int fused_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
                  size_t ws_stats_bytes, uint32_t* counters, size_t counters_bytes, float* out, float* lse,
                  SplitParams* p);
 int launch_fused(const fd_plan_t* plan, const SplitParams& p, void* stream);
+// The stamp records for a launch of `workgroups` workgroups (stamps.hip):
+// null unless the library is the per-workgroup stamp build and they fit.
+uint64_t* wg_stamp_records_for(int64_t workgroups);
 int check_fused_plan(const fd_plan_t* plan);       // FD_OK or the status fd_decode_fused would return
 int record_hip_error(int err, const char* where);  // keeps the text for fd_last_hip_error; FD_ERR_HIP
 

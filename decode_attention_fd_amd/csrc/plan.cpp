@@ -179,6 +179,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   if (o->heuristic != FD_HEURISTIC_MI355X && o->heuristic != FD_HEURISTIC_FA2) return FD_ERR_INVALID_ARG;
   if (!(o->overhead_budget >= 0.0f)) return FD_ERR_INVALID_ARG;
   if (o->piece_cost_tokens < -1 || o->piece_cost_tokens > (1 << 20)) return FD_ERR_INVALID_ARG;
+  if (o->odd_xcd_permille < -1 || o->odd_xcd_permille >= 1000) return FD_ERR_INVALID_ARG;
   if (o->num_host_seq_lens < 0 || (o->num_host_seq_lens > 0 && !o->host_seq_lens)) return FD_ERR_INVALID_ARG;
   if (o->num_host_seq_lens > 0 && o->num_host_seq_lens != prob->batch) return FD_ERR_INVALID_ARG;
   if (o->schedule < FD_SCHEDULE_AUTO || o->schedule > FD_SCHEDULE_BALANCED) return FD_ERR_INVALID_ARG;
@@ -206,6 +207,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   const int64_t paged_align = paged ? (prob->page_size > tile ? prob->page_size : tile) : 1;
 
   int64_t S = 1, chunk = 1;
+  int64_t odd_chunk = -1;               // uniform plans: odd-numbered splits' tokens (-1: chunk)
   int64_t slots = 0;
   int64_t nwg = 0;                      // balanced grid (0: uniform)
   int64_t piece_cost = 0;               // balanced: cost granules per non-empty segment
@@ -350,7 +352,24 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
       chunk = cdiv64(cdiv64(max_len > 0 ? max_len : 1, S), align) * align;
     }
     S = max_len > 0 ? cdiv64(max_len, chunk) : 1;          // drop splits empty for every row
+    // The hardware deals workgroups to the 8 XCDs of a 256-CU MI355X in turn,
+    // so with an even split count split s runs on an XCD of its own parity,
+    // and per-workgroup stamps show the odd XCDs streaming 7-10 % slower than
+    // the even ones, launch after launch (while which half of the chip is
+    // slowest changes from one launch to the next). Odd-numbered splits give
+    // odd_xcd_permille of their tokens to the even-numbered ones; the splits
+    // still cover S * chunk tokens.
+    if (o->heuristic == FD_HEURISTIC_MI355X && !paged && S % 2 == 0 && o->num_cus == 256 &&
+        o->odd_xcd_permille >= 0) {
+      const int64_t x = o->odd_xcd_permille > 0 ? o->odd_xcd_permille : FD_DEFAULT_ODD_XCD_PERMILLE;
+      const int64_t shift = chunk * x / 1000;
+      if (shift > 0 && shift < chunk) {
+        odd_chunk = chunk - shift;
+        chunk += shift;
+      }
+    }
   }
+  if (odd_chunk < 0) odd_chunk = chunk;
   if (S < 1 || S > 65535 || chunk < 1 || chunk > 0x7fffffff) return FD_ERR_UNSUPPORTED;
   // Uniform splits start at s * chunk, a 32-bit token index in the kernels:
   // every split boundary must fit (forced counts and chunks can ask for more).
@@ -360,6 +379,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   out->magic = FD_PLAN_MAGIC;
   out->num_splits = (int32_t)S;
   out->chunk_tokens = (int32_t)chunk;
+  out->odd_chunk_tokens = (int32_t)odd_chunk;
   out->kernel = kernel;
   out->ws_format = o->ws_format;
   out->group = g;

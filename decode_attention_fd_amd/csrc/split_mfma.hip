@@ -45,6 +45,7 @@
 #include "geometry.h"
 #include "merge_rows.h"
 #include "balance.h"
+#include "stamps.h"
 
 namespace fd {
 namespace {
@@ -444,31 +445,39 @@ __device__ __forceinline__ void split_piece(const SplitParams& p, Smem<D>& sm, i
 template <int D, typename T, bool PAGED, int NCT>
 __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitParams p) {
   __shared__ Smem<D> sm;
+  WgStamp stamp;
+  stamp_begin(p, stamp);
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   int seq_len = p.seq_lens[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > p.cap_tokens ? p.cap_tokens : seq_len);
-  // Split s covers [s*chunk, s*chunk + chunk) clamped to the sequence; formed
-  // in 64 bits (the plan bounds S*chunk by INT32_MAX, but a start past the
-  // sequence must never wrap to a negative token index).
-  const int64_t s0 = (int64_t)s * p.chunk;
+  // Split s covers [s0, s0 + len) clamped to the sequence, with even- and
+  // odd-numbered splits of chunk and chunk_odd tokens; formed in 64 bits (the
+  // plan bounds the splits' end by INT32_MAX, but a start past the sequence
+  // must never wrap to a negative token index).
+  const int64_t s0 = (int64_t)(s >> 1) * (p.chunk + p.chunk_odd) + ((s & 1) ? p.chunk : 0);
+  const int64_t len = (s & 1) ? p.chunk_odd : p.chunk;
   const int start = (int)(s0 < seq_len ? s0 : seq_len);
-  const int end = (int)(s0 + p.chunk < seq_len ? s0 + p.chunk : seq_len);
+  const int end = (int)(s0 + len < seq_len ? s0 + len : seq_len);
   const bool direct = p.fused && p.S == 1;
-  if (end > start)
+  if (end > start) {
     split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, s, seq_len - (p.q_len - 1), direct);
-  else if (direct)
+    stamp_piece(stamp, end - start);
+  } else if (direct)
     empty_group<D, NW * 64>(p, b, kvh);
   else
     write_neutral<D, NW * 64>(p, b, kvh, s, s + 1);
   if (p.fused && !direct) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, p.S);
+  stamp_end(p, stamp);
 }
 
 // Balanced schedule: workgroup w owns an equal share of the batch's granules.
 template <int D, typename T, bool PAGED, int NCT>
 __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParams p) {
   __shared__ Smem<D> sm;
+  WgStamp stamp;
+  stamp_begin(p, stamp);
   balanced_walk<NW * 64>(
       p,
       [&](int b, int kvh, int start, int end, int slot, int count, bool last, int len) {
@@ -480,6 +489,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
         if (slot >= p.S) return;                 // lengths differ from the plan's: write nothing
         const bool direct = p.fused && count == 1;
         split_piece<D, T, PAGED, NCT>(p, sm, b, kvh, start, end, slot, len - (p.q_len - 1), direct);
+        stamp_piece(stamp, end - start);
         if (!direct) {
           if (last) write_neutral<D, NW * 64>(p, b, kvh, slot + 1, p.S);
           if (p.fused) fused_group_merge<D, NW * 64, FUSED_BATCH>(p, b, kvh, count < p.S ? count : p.S);
@@ -487,6 +497,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_balanced_kernel(SplitParam
         __syncthreads();                         // LDS is reused by the next piece
       },
       [&](int b) { empty_row<D, NW * 64>(p, b); });
+  stamp_end(p, stamp);
 }
 
 template <int D, typename T, bool PAGED>

@@ -111,7 +111,8 @@ typedef enum {
    * in use; else UNIFORM. */
   FD_SCHEDULE_AUTO = 0,
   /* One workgroup per (split, KV head, sequence); split s of every segment is
-   * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1). */
+   * [s*chunk, s*chunk + chunk) (kanthi.in §4 kernel 1), or with alternating
+   * even and odd lengths (fd_plan_t::chunk_tokens, odd_chunk_tokens). */
   FD_SCHEDULE_UNIFORM = 1,
   /* Needs host_seq_lens. The batch's (sequence, KV head) segments, each cut
    * into granules of G tokens (G = the wave tile, or the page if larger), are
@@ -140,6 +141,10 @@ typedef enum {
  * fd_merge_states): merge grids are indexed in 32 bits. A larger problem is
  * FD_ERR_UNSUPPORTED. */
 #define FD_MAX_ROWS ((int64_t)0x7fffffff - 4096)
+
+/* Default shift of tokens from odd-XCD to even-XCD splits, per mille
+ * (fd_plan_opts::odd_xcd_permille). */
+#define FD_DEFAULT_ODD_XCD_PERMILLE 45
 
 /* Default start-up cost of one balanced piece, in KV tokens. */
 #define FD_DEFAULT_PIECE_COST_TOKENS 512
@@ -201,7 +206,12 @@ typedef struct {
   int32_t piece_cost_tokens;  /* balanced schedule: start-up cost of one piece, in KV tokens, added
                                  to every non-empty segment when the line is cut
                                  (0: FD_DEFAULT_PIECE_COST_TOKENS; -1: none) */
-  int32_t reserved[4];
+  int32_t odd_xcd_permille;   /* uniform plans the MI355X rule makes (not forced), contiguous cache,
+                                 even split count, 256 CUs: odd-numbered splits, which the hardware
+                                 places on the odd XCDs, get 1000 - x tokens per 1000 of an even
+                                 split's 1000 + x, against the odd XCDs' slower streaming
+                                 (0: FD_DEFAULT_ODD_XCD_PERMILLE; -1: equal splits) */
+  int32_t reserved[3];
   /* Optional HOST copy of seq_lens (int32 [batch]). With it the MI355X rule
    * sizes splits from the batch's total work: no split longer than one
    * slot's share, cdiv(Hkv * sum(len), slots) tokens, so a ragged batch is
@@ -215,7 +225,10 @@ typedef struct {
 typedef struct {
   uint32_t magic;             /* FD_PLAN_MAGIC */
   int32_t num_splits;         /* S >= 1 */
-  int32_t chunk_tokens;       /* split s covers [s*chunk, min(s*chunk + chunk, seq_len)) */
+  int32_t chunk_tokens;       /* UNIFORM: split s covers [start_s, min(start_s + len_s, seq_len)) with
+                                 len_s = chunk_tokens for even s, odd_chunk_tokens for odd s, and
+                                 start_s = (s / 2) (chunk_tokens + odd_chunk_tokens) + (s odd ?
+                                 chunk_tokens : 0): with equal lengths, [s*chunk, s*chunk + chunk) */
   int32_t kernel;             /* fd_kernel actually used (never AUTO) */
   int32_t ws_format;          /* fd_ws_format */
   int32_t group;              /* g = Hq / Hkv */
@@ -228,7 +241,8 @@ typedef struct {
                                  chunk_tokens is the granule G, grid (N, 1, 1), and S is the
                                  largest number of pieces any (b, kv head) segment is cut into */
   int32_t piece_cost;         /* BALANCED: granules of start-up cost added per non-empty segment */
-  int32_t reserved2;
+  int32_t odd_chunk_tokens;   /* UNIFORM: tokens of an odd-numbered split; chunk_tokens is an
+                                 even-numbered split's (equal unless odd_xcd_permille shifted them) */
   int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
   int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
   int64_t ws_counter_bytes;   /* uint32 [B, Hkv] arrival counters of fd_decode_fused */
@@ -336,6 +350,18 @@ FD_API int fd_merge_states(int ws_format, const float* states, const float* stat
  * nothing else. Time it with events on `stream`. */
 #define FD_READ_PROBE_SINK_BYTES (512 * 256 * 4)
 FD_API int fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream);
+
+/* Measurement aid, not part of the attention path. A build with per-workgroup
+ * stamps (decode_attention_fd_amd/build.py --wg-stamps) records, in every
+ * split-kernel launch of at most FD_WG_STAMP_RECORDS workgroups, four uint64
+ * per workgroup w (linear index over the grid x, y, z): its start and end on
+ * the device's 100 MHz constant clock, the K/V tokens it streamed, and its
+ * piece count | its XCD id << 32. fd_wg_stamps copies the records of the
+ * current device (the last launch's, for the workgroups it had) into device
+ * memory dst (dst_bytes, at most FD_WG_STAMP_RECORDS * 32 bytes are copied)
+ * on stream. Other builds record nothing and return FD_ERR_UNSUPPORTED. */
+#define FD_WG_STAMP_RECORDS 65536
+FD_API int fd_wg_stamps(void* dst, size_t dst_bytes, void* stream);
 
 /* Human-readable text for an fd_status. Never NULL. */
 FD_API const char* fd_status_str(int status);

@@ -176,6 +176,22 @@ def chunk_bounds(seq_len: int, chunk: int, num_splits: int) -> List[Tuple[int, i
     return out
 
 
+def alternating_bounds(seq_len: int, even_chunk: int, odd_chunk: int, num_splits: int) -> List[Tuple[int, int]]:
+    """The partition of chunk_bounds with two alternating lengths: split s
+    holds even_chunk tokens for even s and odd_chunk for odd s, starting where
+    split s - 1 ends, clipped at seq_len; a split starting at or past seq_len
+    is empty and is returned as (start, start). Any contiguous partition
+    merges to the same result ([KANTHI] §2); this one lets the splits that
+    run on slower hardware units hold fewer tokens."""
+    out = []
+    a = 0
+    for s in range(num_splits):
+        n = even_chunk if s % 2 == 0 else odd_chunk
+        out.append((a, max(a, min(a + n, seq_len))))
+        a += n
+    return out
+
+
 def linspace_bounds(total: int, num_splits: int) -> List[int]:
     """Uneven boundaries ``linspace(0, T, S+1)`` truncated to int ([KANTHI] §3)."""
     return np.linspace(0, total, num_splits + 1).astype(int).tolist()

@@ -9,4 +9,5 @@ int launch_split_mfma(const SplitParams&, int, int, int, void*) { return 1; }
 int launch_split_valu(const SplitParams&, int, int, int, int, void*) { return 1; }
 int occupancy_split_mfma(int, int, int, int, int* o) { *o = 1; return 0; }
 int occupancy_split_valu(int, int, int, int, int* o) { *o = 1; return 0; }
+uint64_t* wg_stamp_records_for(int64_t) { return nullptr; }
 }

@@ -96,6 +96,22 @@ def test_fa2_heuristic_reproduces_page_table():
         assert plan.slots == g["slots"]
 
 
+def base_chunk(plan, paged=False, cus=256):
+    """The split rule's chunk of a uniform plan, after checking the odd-XCD
+    shift: with an even split count on a 256-CU device (contiguous cache),
+    even-numbered splits hold chunk + shift and odd ones chunk - shift tokens,
+    shift = chunk * FD_DEFAULT_ODD_XCD_PERMILLE // 1000; else both chunk."""
+    c, c_odd, S = plan.chunk_tokens, plan.odd_chunk_tokens, plan.num_splits
+    assert (c + c_odd) % 2 == 0
+    base = (c + c_odd) // 2
+    shift = base * 45 // 1000
+    if not paged and S % 2 == 0 and cus == 256 and 0 < shift < base:
+        assert (c, c_odd) == (base + shift, base - shift), (S, c, c_odd)
+    else:
+        assert c == c_odd, (S, c, c_odd)
+    return base
+
+
 @pytest.mark.parametrize("kernel", ["mfma", "valu"])
 @pytest.mark.parametrize("wgs", [1, 2])
 def test_mi355x_heuristic_matches_oracle_rule(kernel, wgs):
@@ -112,7 +128,7 @@ def test_mi355x_heuristic_matches_oracle_rule(kernel, wgs):
                 s = OP.num_splits_traffic(B * Hkv, cus * wgs, math.ceil(L / block), 128, g, 128, 2, L, budget,
                                           threshold=1.0)
                 chunk = OP.chunk_for(L, s, 1)              # contiguous: cdiv(L, S), no tile rounding
-                assert plan.chunk_tokens == chunk, (B, Hkv, g, L)
+                assert base_chunk(plan) == chunk, (B, Hkv, g, L)
                 assert plan.num_splits == math.ceil(L / chunk), (B, Hkv, g, L)
                 assert plan.num_splits <= s
 
@@ -121,7 +137,18 @@ def test_mi355x_choices_for_the_workloads():
     """The planner's picks for the four large workloads (256 CUs, defaults)."""
     assert fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256).num_splits == 32
     p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256)
-    assert p.chunk_tokens == 4000 and p.slots == 256
+    assert base_chunk(p) == 4000 and p.slots == 256
+    assert (p.chunk_tokens, p.odd_chunk_tokens) == (4180, 3820)     # 4.5 % from odd-XCD splits to even ones
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, odd_xcd_permille=-1)
+    assert (p.num_splits, p.chunk_tokens, p.odd_chunk_tokens) == (32, 4000, 4000)
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, odd_xcd_permille=100)
+    assert (p.chunk_tokens, p.odd_chunk_tokens) == (4400, 3600)
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=128)
+    assert p.chunk_tokens == p.odd_chunk_tokens                      # not the 256-CU device
+    p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, force_splits=32)
+    assert p.chunk_tokens == p.odd_chunk_tokens == 4000               # forced plans keep equal splits
+    assert _status(contiguous_problem(), odd_xcd_permille=1000) == fd.FD_ERR_INVALID_ARG
+    assert _status(contiguous_problem(), odd_xcd_permille=-2) == fd.FD_ERR_INVALID_ARG
     assert fd.fd_plan(contiguous_problem(B=64, Hq=32, Hkv=8, L=2048), num_cus=256).num_splits == 1
     assert fd.fd_plan(contiguous_problem(Hq=32, Hkv=32, L=65536, dtype=2), num_cus=256).num_splits == 8
 
@@ -143,7 +170,7 @@ def test_length_aware_rule_matches_oracle(paged):
         plan = fd.fd_plan(prob, num_cus=256, kernel=kernel, host_seq_lens=lens.tolist(), schedule="uniform")
         align = max(plan.tile_tokens, 16) if paged else 1
         chunk = OP.chunk_from_lengths(lens.tolist(), L, Hkv, 256, align, 128, g, 128, 2, 0.25)
-        assert plan.chunk_tokens == chunk, (B, Hkv, g, L, lens.tolist()[:4])
+        assert base_chunk(plan, paged) == chunk, (B, Hkv, g, L, lens.tolist()[:4])
         assert plan.num_splits == math.ceil(L / chunk)
 
 
@@ -152,7 +179,7 @@ def test_length_aware_choices():
     its total work, not by its longest row."""
     p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, host_seq_lens=[128000],
                    schedule="uniform")
-    assert (p.num_splits, p.chunk_tokens) == (32, 4000)
+    assert (p.num_splits, base_chunk(p)) == (32, 4000)
     lens = [32768] + [1024] * 15
     p = fd.fd_plan(paged_problem(B=16, L=32768), num_cus=256, host_seq_lens=lens, schedule="uniform")
     assert p.chunk_tokens == OP.cdiv(OP.cdiv(8 * sum(lens), 256), 32) * 32

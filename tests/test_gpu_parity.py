@@ -45,6 +45,33 @@ def test_tiny_partial_states_match_oracle_splits(fmt):
                 assert abs(l_s[0, h, s] - L[0, h, s]) < 1e-5 * L[0, h, s]
 
 
+@pytest.mark.parametrize("fmt", ["uml", "olse"])
+def test_odd_xcd_shifted_plan_states(fmt):
+    """A uniform plan the MI355X rule shifts (even split count, contiguous cache,
+    256 CUs): even-numbered splits hold chunk_tokens tokens and odd-numbered
+    ones odd_chunk_tokens. Every split state of sampled rows against the
+    oracle's states over the same alternating partition, and every output."""
+    w = W.contiguous("xcd_shift", seed=120, batch=2, q_heads=64, kv_heads=8, head_dim=128, capacity=20000,
+                     seq_lens=[20000, 13001], dtype="f16")
+    plan, out, lse, ws_o, ws_stats = H.run(w, ws_format=fmt, schedule="uniform")
+    H.say(f"shifted plan: S={plan.num_splits} chunks {plan.chunk_tokens}/{plan.odd_chunk_tokens}")
+    assert plan.num_splits % 2 == 0 and plan.chunk_tokens > plan.odd_chunk_tokens
+    H.check_against_oracle(w, out, lse)
+    pairs = [(0, 0), (0, 37), (1, 5), (1, 63)]
+    bounds = lambda b, h: A.alternating_bounds(int(w.seq_lens[b]), plan.chunk_tokens, plan.odd_chunk_tokens,
+                                               plan.num_splits)
+    M, L, U = A.split_states(H.cache_of(w), plan.num_splits, 0, pairs=pairs, bounds=bounds)
+    o_s, lse_s, m_s, l_s = H.split_states_of(plan, ws_o, ws_stats)
+    for b, h in pairs:
+        for s in range(plan.num_splits):
+            if L[b, h, s] == 0:
+                assert np.isneginf(lse_s[b, h, s]) and np.all(o_s[b, h, s] == 0)
+                continue
+            o_ref, lse_ref = A.state_to_olse(M[b, h, s], L[b, h, s], U[b, h, s])
+            assert np.abs(o_s[b, h, s] - o_ref).max() < 2e-3, (b, h, s)
+            assert abs(lse_s[b, h, s] - lse_ref) < 1e-5 * max(1, abs(lse_ref)), (b, h, s)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("q_gain", [1.0, 40.0])
 def test_ragged_batch_with_empty_splits(splits, q_gain):

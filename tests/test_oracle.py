@@ -266,6 +266,27 @@ def test_pages_split_reference_in_f64():
 # Empty / fully masked splits (kanthi §4; xuujii §06)
 # ---------------------------------------------------------------------------
 
+def test_alternating_bounds_by_hand_and_against_chunk_bounds():
+    """By hand: 10 tokens in four splits of 4, 2, 4, 2 tokens end at 4, 6, 10 and
+    start the fourth at 10 (empty); 7 tokens clip the third split to [6, 7).
+    Equal lengths give chunk_bounds' partition; any lengths tile [0, len)
+    in order."""
+    assert A.alternating_bounds(10, 4, 2, 4) == [(0, 4), (4, 6), (6, 10), (10, 10)]
+    assert A.alternating_bounds(7, 4, 2, 4) == [(0, 4), (4, 6), (6, 7), (10, 10)]
+    assert A.alternating_bounds(0, 3, 5, 2) == [(0, 0), (3, 3)]
+    for L in (0, 1, 37, 999, 1000, 1001):
+        for S, c in ((3, 334), (8, 125), (32, 40)):
+            assert A.alternating_bounds(L, c, c, S) == A.chunk_bounds(L, c, S)
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        S = int(rng.integers(1, 20))
+        ce, co = int(rng.integers(1, 50)), int(rng.integers(1, 50))
+        L = int(rng.integers(0, (S // 2) * (ce + co) + (S % 2) * ce + 1))
+        b = A.alternating_bounds(L, ce, co, S)
+        covered = [t for lo, hi in b for t in range(lo, hi)]
+        assert covered == list(range(L))
+
+
 def test_chunk_bounds_ragged_table():
     g = golden("split_reference.json")["ragged"]
     assert -(-g["T_max"] // g["num_splits"]) == g["chunk"]
