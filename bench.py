@@ -208,11 +208,13 @@ def wg_stamp_report(plan, launch, launches: int, torch, fd, stream) -> dict:
         torch.cuda.synchronize()
         r = buf[:4 * nwg].view(nwg, 4).cpu().numpy().astype(np.int64)
         t0 = r[:, 0].min()
-        recs.append(np.stack([r[:, 0] - t0, r[:, 1] - t0, r[:, 2], r[:, 3] & 0xFFFFFFFF, r[:, 3] >> 32], 1))
-    a = np.stack(recs)                                 # [launch, wg, (start, end, tokens, pieces, xcc)] in 10 ns ticks
+        recs.append(np.stack([r[:, 0] - t0, r[:, 1] - t0, r[:, 2], r[:, 3] & 0xFFFFFFFF, (r[:, 3] >> 32) & 0xFF,
+                              (r[:, 3] >> 40) & 0xFF], 1))
+    a = np.stack(recs)                          # [launch, wg, (start, end, tokens, pieces, xcc, place)]; 10 ns ticks
     start_us, end_us = a[..., 0] / 100.0, a[..., 1] / 100.0
     dur_us = end_us - start_us
     tokens, pieces, xcc = a[..., 2], a[..., 3], a[..., 4]
+    cu = xcc * 256 + a[..., 5]                  # one id per CU of the device
     q = lambda x: [round(float(v), 2) for v in np.percentile(x, [0, 10, 50, 90, 100])]
     out = {"workgroups": int(nwg), "launches": int(launches),
            "end_us_min_p10_p50_p90_max": q(end_us), "duration_us_min_p10_p50_p90_max": q(dur_us),
@@ -251,6 +253,37 @@ def wg_stamp_report(plan, launch, launches: int, torch, fd, stream) -> dict:
                                                round(float(end_us[i][odd[i]].mean()), 2)] for i in range(launches)]
     out["per_launch_max_end_us_even_odd"] = [[round(float(end_us[i][~odd[i]].max()), 2),
                                               round(float(end_us[i][odd[i]].max()), 2)] for i in range(launches)]
+    # Does a workgroup's lateness follow its range (the data it reads) or its
+    # CU? Lateness = end minus the launch's mean end. Mean lateness per range
+    # and per CU over the even launches against the odd launches: a Pearson r
+    # near 1 means it repeats from launch to launch.
+    late = end_us - end_us.mean(axis=1, keepdims=True)
+    out["same_cu_as_first_launch"] = round(float(np.mean(cu == cu[:1])), 4)
+    out["distinct_cus"] = int(len(set(cu.ravel().tolist())))
+
+    def repeat(key):
+        halves = []
+        for sel in (slice(0, None, 2), slice(1, None, 2)):
+            k, v = key[sel].ravel(), late[sel].ravel()
+            sums, counts = {}, {}
+            for kk, vv in zip(k.tolist(), v.tolist()):
+                sums[kk] = sums.get(kk, 0.0) + vv
+                counts[kk] = counts.get(kk, 0) + 1
+            halves.append({kk: sums[kk] / counts[kk] for kk in sums})
+        common = sorted(set(halves[0]) & set(halves[1]))
+        x = np.array([halves[0][kk] for kk in common])
+        y = np.array([halves[1][kk] for kk in common])
+        r = float(np.corrcoef(x, y)[0, 1]) if len(common) > 2 and x.std() > 0 and y.std() > 0 else float("nan")
+        return {"pearson_r_even_vs_odd_launches": round(r, 3), "keys": len(common),
+                "lateness_sd_us": round(float(np.concatenate([x, y]).std()), 2)}
+
+    out["lateness_repeats_by_range"] = repeat(np.broadcast_to(lin[None, :], end_us.shape))
+    out["lateness_repeats_by_cu"] = repeat(cu)
+    out["lateness_sd_us_within_launch"] = round(float(late.std()), 2)
+    if launches >= 2 and nwg <= 4096:
+        keys = sorted(set(cu.ravel().tolist()))
+        out["mean_lateness_us_by_cu"] = {int(k): round(float(late[cu == k].mean()), 2) for k in keys}
+        out["cu_of_workgroup_first_launch"] = [int(c) for c in cu[0]]
     return out
 
 
@@ -648,6 +681,7 @@ def main():
             "kv_bytes_allocated": alloc, "kv_copies": copies, "layout": "paged" if w0.paged else "contiguous",
             "num_splits": plan.num_splits, "chunk_tokens": plan.chunk_tokens,
             "odd_chunk_tokens": plan.odd_chunk_tokens,
+            "odd_range_permille": plan.odd_range_permille,
             "kernel": {1: "mfma", 2: "valu"}[plan.kernel], "ws_format": {0: "uml", 1: "olse"}[plan.ws_format],
             "slots": plan.slots, "plan_us": round(plan_us, 1), "plan_first_us": round(plan_first_us, 1), "path": path,
             "schedule": {1: "uniform", 2: "balanced"}[plan.schedule], "grid": plan.grid_x * plan.grid_y * plan.grid_z,

@@ -69,6 +69,7 @@ class Plan(ctypes.Structure):
         ("grid_x", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32),
         ("scale", ctypes.c_float), ("schedule", ctypes.c_int32),
         ("piece_cost", ctypes.c_int32), ("odd_chunk_tokens", ctypes.c_int32),
+        ("odd_range_permille", ctypes.c_int32), ("reserved3", ctypes.c_int32),
         ("ws_o_bytes", ctypes.c_int64), ("ws_stats_bytes", ctypes.c_int64), ("ws_counter_bytes", ctypes.c_int64),
         ("prob", Problem), ("checksum", ctypes.c_uint64),
     ]

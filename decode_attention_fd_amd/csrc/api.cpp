@@ -102,6 +102,9 @@ int check_plan(const fd_plan_t* plan) {
   if (plan->num_splits < 1 || plan->chunk_tokens < 1 || plan->odd_chunk_tokens < 1) return FD_ERR_BAD_PLAN;
   if (plan->schedule != FD_SCHEDULE_UNIFORM && plan->schedule != FD_SCHEDULE_BALANCED) return FD_ERR_BAD_PLAN;
   if (plan->schedule == FD_SCHEDULE_BALANCED && (plan->grid_x < 1 || plan->piece_cost < 0)) return FD_ERR_BAD_PLAN;
+  if (plan->odd_range_permille < 0 || plan->odd_range_permille > 999 ||
+      (plan->schedule != FD_SCHEDULE_BALANCED && plan->odd_range_permille != 0))
+    return FD_ERR_BAD_PLAN;
   return FD_OK;
 }
 
@@ -240,6 +243,7 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
     p.nwg = plan->grid_x;
     p.granule = plan->chunk_tokens;
     p.piece_cost = plan->piece_cost;
+    p.range_odd = plan->odd_range_permille;
   } else {
     // Tokens past the last split belong to no split: clamp there as well.
     const int64_t covered = (int64_t)(plan->num_splits / 2) * (plan->chunk_tokens + plan->odd_chunk_tokens) +

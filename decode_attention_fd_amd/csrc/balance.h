@@ -14,7 +14,12 @@
 // latency, epilogue), so a range of many short segments gets fewer tokens;
 // segments are in (b, h) order. A grid of N
 // workgroups cuts that line into N near-equal ranges, workgroup w taking
-// granules [floor(w T / N), floor((w + 1) T / N)) of the T in total. A range
+// granules [floor(w T / N), floor((w + 1) T / N)) of the T in total; or, with
+// x = p.range_odd > 0, ranges of alternating size: w takes 1000 + x (w even)
+// or 1000 - x (w odd) parts per 1000 of an equal share, starting at
+// floor(c_w T / c_N) with c_w the parts of ranges 0 .. w-1, so that the odd
+// XCDs (workgroup w runs on XCD w mod 8), which stream more slowly, get
+// less. A range
 // may cover the end of one segment and the start of the next; each part of a
 // segment it covers is one "piece" and yields one attention state, stored at
 // slot w - first(segment) of that segment's rows, where first(x) is the
@@ -85,9 +90,25 @@ __device__ __forceinline__ void empty_row(const SplitParams& p, int b) {
   }
 }
 
-// Workgroup owning granule x of a line of `total` granules cut into `nwg` ranges.
-__device__ __forceinline__ int64_t granule_owner(int64_t x, int64_t total, int64_t nwg) {
-  return ((x + 1) * nwg + total - 1) / total - 1;
+// Parts of ranges 0 .. w-1 when range w has 1000 + x (w even) or 1000 - x (w odd).
+__device__ __forceinline__ int64_t range_parts(int64_t w, int64_t x) {
+  return (w >> 1) * 2000 + ((w & 1) ? 1000 + x : 0);
+}
+
+// First granule of range w of a line of `total` granules cut into `nwg` ranges.
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nwg, int64_t x) {
+  return x == 0 ? w * total / nwg : range_parts(w, x) * total / range_parts(nwg, x);
+}
+
+// Workgroup owning granule g: the last range w with range_start(w) <= g. With
+// M = range_parts(nwg), floor(c_w total / M) <= g holds exactly when
+// c_w <= ceil((g + 1) M / total) - 1 =: c; the last w with c_w <= c is 2 (c div
+// 2000), plus one when c mod 2000 reaches an even range's 1000 + x.
+__device__ __forceinline__ int64_t granule_owner(int64_t g, int64_t total, int64_t nwg, int64_t x) {
+  if (x == 0) return ((g + 1) * nwg + total - 1) / total - 1;
+  const int64_t c = ((g + 1) * range_parts(nwg, x) + total - 1) / total - 1;
+  const int64_t w = 2 * (c / 2000) + (c % 2000 >= 1000 + x ? 1 : 0);
+  return w < nwg - 1 ? w : nwg - 1;
 }
 
 __device__ __forceinline__ int clamp_len(const SplitParams& p, int b) {
@@ -157,8 +178,8 @@ __device__ BalancedStart balanced_start(const SplitParams& p, BalancedLds<NTHREA
   }
   const int64_t nwg = gridDim.x;
   const int64_t w = blockIdx.x;
-  const int64_t gs = w * total / nwg;
-  const int64_t ge = (w + 1) * total / nwg;
+  const int64_t gs = range_start(w, total, nwg, p.range_odd);
+  const int64_t ge = range_start(w + 1, total, nwg, p.range_odd);
 
   int64_t x = before + incl - local;   // start of row r0
   int cand = B;
@@ -228,9 +249,9 @@ __device__ __forceinline__ void balanced_walk(const SplitParams& p, Piece&& piec
       if (se <= st.gs) continue;                         // only its cost granules fall in this range
       const int64_t ps = ss > st.gs ? ss : st.gs;
       const int64_t pe = se < st.ge ? se : st.ge;
-      const int64_t first = granule_owner(ss, st.total, nwg);
+      const int64_t first = granule_owner(ss, st.total, nwg, p.range_odd);
       const int slot = (int)(w - first);
-      const int count = (int)(granule_owner(se - 1, st.total, nwg) - first + 1);
+      const int count = (int)(granule_owner(se - 1, st.total, nwg, p.range_odd) - first + 1);
       const int64_t t1 = (pe - ss) * G;
       piece(b, h, (int)((ps - ss) * G), (int)(t1 < len ? t1 : len), slot, count, se <= st.ge, len);
     }

@@ -58,6 +58,7 @@ struct SplitParams {
   int32_t nwg;                          // workgroups of the balanced grid
   int32_t granule;                      // tokens per granule of the balanced line
   int32_t piece_cost;                   // cost granules after each non-empty segment on the line
+  int32_t range_odd;                    // alternating range sizes, parts per mille (0: equal ranges)
   // fused merge (0 = write split states only)
   int32_t fused;
   uint32_t* counters;                   // [B * Hkv], zero on entry, zero on exit

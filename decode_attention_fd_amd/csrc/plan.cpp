@@ -211,6 +211,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   int64_t slots = 0;
   int64_t nwg = 0;                      // balanced grid (0: uniform)
   int64_t piece_cost = 0;               // balanced: cost granules per non-empty segment
+  int64_t odd_range = 0;                // balanced: alternating range sizes, per mille
   // AUTO takes the balanced schedule where it pays: ragged lengths (equal
   // lengths are already balanced by the uniform chunks) whose mean is at
   // least FD_BALANCED_MIN_MEAN_TOKENS. A balanced workgroup runs its pieces
@@ -268,13 +269,38 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
       // The kernels rebuild the line from the device lengths (clamped to the
       // capacity) and form products of granule positions with the grid size
       // in 64 bits: bound the longest line any device lengths could give.
-      {
-        const int64_t cap = prob->layout == FD_LAYOUT_PAGED ? (int64_t)prob->max_pages_per_seq * prob->page_size
-                                                            : (int64_t)prob->kv_capacity;
-        const int64_t t_max = (int64_t)prob->batch * H * (cdiv64(cap, G) + piece_cost);
-        if (t_max > ((int64_t)1 << 62) / (nwg + 1)) return FD_ERR_UNSUPPORTED;
+      const int64_t cap = prob->layout == FD_LAYOUT_PAGED ? (int64_t)prob->max_pages_per_seq * prob->page_size
+                                                          : (int64_t)prob->kv_capacity;
+      const int64_t t_max = (int64_t)prob->batch * H * (cdiv64(cap, G) + piece_cost);
+      if (t_max > ((int64_t)1 << 62) / (nwg + 1)) return FD_ERR_UNSUPPORTED;
+      // Ranges of alternating size against the odd XCDs' slower streaming
+      // (workgroup w runs on XCD w mod 8; the uniform rule below says more):
+      // odd ranges take 1000 - x parts per 1000 of an equal share, even ones
+      // 1000 + x. Only where ranges are long enough to be bound by streaming:
+      // per-workgroup stamps of the 64-sequence edge batch (about 2100 tokens
+      // per range, several pieces each) show no odd-XCD lag, those of the
+      // paged ragged batch (about 10 000 per range) a 7 % one. The weighted
+      // cut multiplies granule positions by about 1000 N. Every odd range
+      // keeps at least one granule ((1000 - x) T >= 1000 N): the piece count
+      // of a segment is the difference of its end and start owners, which
+      // holds only while no range is empty.
+      int64_t xr = 0;
+      if (o->heuristic == FD_HEURISTIC_MI355X && o->num_cus == 256 && o->odd_xcd_permille >= 0 && nwg % 8 == 0 &&
+          H * len_sum >= (int64_t)FD_XCD_SHIFT_MIN_RANGE_TOKENS * nwg &&
+          t_max <= ((int64_t)1 << 62) / (1000 * (nwg + 2))) {
+        xr = o->odd_xcd_permille > 0 ? o->odd_xcd_permille : FD_DEFAULT_ODD_XCD_PERMILLE;
+        if ((1000 - xr) * T < 1000 * nwg) xr = 0;
       }
-      auto owner = [&](int64_t x) { return ((x + 1) * nwg + T - 1) / T - 1; };
+      odd_range = xr;
+      const int64_t parts_all = (nwg / 2) * 2000 + (nwg % 2 ? 1000 + xr : 0);
+      // Owner of granule x: the last range starting at or before it (range w
+      // starts at floor(c_w T / c_N), c_w the parts of ranges 0 .. w-1).
+      auto owner = [&](int64_t x) {
+        if (xr == 0) return ((x + 1) * nwg + T - 1) / T - 1;
+        const int64_t c = ((x + 1) * parts_all + T - 1) / T - 1;
+        const int64_t w = 2 * (c / 2000) + (c % 2000 >= 1000 + xr ? 1 : 0);
+        return w < nwg - 1 ? w : nwg - 1;
+      };
       S = 1;
       int64_t x = 0;
       for (int b = 0; b < prob->batch; ++b) {
@@ -388,6 +414,7 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
   out->slots = (int32_t)slots;
   out->schedule = nwg > 0 ? FD_SCHEDULE_BALANCED : FD_SCHEDULE_UNIFORM;
   out->piece_cost = (int32_t)piece_cost;
+  out->odd_range_permille = (int32_t)odd_range;
   out->grid_x = nwg > 0 ? (int32_t)nwg : (int32_t)S;
   out->grid_y = nwg > 0 ? 1 : prob->num_kv_heads;
   out->grid_z = nwg > 0 ? 1 : prob->batch;

@@ -1,7 +1,8 @@
 // Per-workgroup stamps of the split kernels, compiled in only by the
 // measurement build (FD_WG_STAMPS; build.py --wg-stamps): for each workgroup,
 // its start and end on the device's 100 MHz constant clock, the K/V tokens it
-// streamed, the pieces it ran and the XCD it ran on. Read back with
+// streamed, the pieces it ran, the XCD it ran on and its place inside the
+// XCD (shader engine, shader array, CU). Read back with
 // fd_wg_stamps. In the release build every hook below is empty.
 #pragma once
 
@@ -32,11 +33,13 @@ __device__ __forceinline__ void stamp_end(const SplitParams& p, const WgStamp& s
   if (threadIdx.x == 0) {
     const uint64_t w = blockIdx.x + (uint64_t)gridDim.x * (blockIdx.y + (uint64_t)gridDim.y * blockIdx.z);
     const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 0xfu;   // HW_REG_XCC_ID
+    // HW_REG_HW_ID bits 8..15: CU id (4 bits), shader array (1), shader engine (3)
+    const unsigned place = __builtin_amdgcn_s_getreg(4 | (8 << 6) | (7 << 11)) & 0xffu;
     uint64_t* rec = p.stamps + 4 * w;
     rec[0] = s.t0;
     rec[1] = wall_clock64();
     rec[2] = (uint64_t)s.tokens;
-    rec[3] = (uint64_t)s.pieces | ((uint64_t)xcc << 32);
+    rec[3] = (uint64_t)s.pieces | ((uint64_t)xcc << 32) | ((uint64_t)place << 40);
   }
 }
 #else

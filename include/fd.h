@@ -123,7 +123,11 @@ typedef enum {
    * caller sets it, and cdiv(total granules, 4))). A segment crossing a range
    * boundary yields one state per range: a Stream-K-style partition of the
    * kind kanthi.in §7 lists (LeanAttention) against wave quantization, here
-   * so that every workgroup streams the same number of bytes. */
+   * so that every workgroup streams the same number of bytes. With
+   * fd_plan_t::odd_range_permille = x > 0 the ranges alternate in size:
+   * range w takes 1000 + x (w even) or 1000 - x (w odd) parts per 1000 of an
+   * equal share, range w starting at granule floor(c_w T / c_N) where c_w is
+   * the sum of the parts of ranges 0 .. w-1. */
   FD_SCHEDULE_BALANCED = 2
 } fd_schedule;
 
@@ -145,6 +149,12 @@ typedef enum {
 /* Default shift of tokens from odd-XCD to even-XCD splits, per mille
  * (fd_plan_opts::odd_xcd_permille). */
 #define FD_DEFAULT_ODD_XCD_PERMILLE 45
+
+/* The balanced schedule shifts work from odd-XCD ranges only when a range
+ * averages at least this many tokens of K/V rows (KV heads x tokens / N):
+ * shorter ranges are bound by their pieces' start-up latencies, not by the
+ * XCD's streaming rate. */
+#define FD_XCD_SHIFT_MIN_RANGE_TOKENS 4096
 
 /* Default start-up cost of one balanced piece, in KV tokens. */
 #define FD_DEFAULT_PIECE_COST_TOKENS 512
@@ -206,11 +216,15 @@ typedef struct {
   int32_t piece_cost_tokens;  /* balanced schedule: start-up cost of one piece, in KV tokens, added
                                  to every non-empty segment when the line is cut
                                  (0: FD_DEFAULT_PIECE_COST_TOKENS; -1: none) */
-  int32_t odd_xcd_permille;   /* uniform plans the MI355X rule makes (not forced), contiguous cache,
-                                 even split count, 256 CUs: odd-numbered splits, which the hardware
-                                 places on the odd XCDs, get 1000 - x tokens per 1000 of an even
-                                 split's 1000 + x, against the odd XCDs' slower streaming
-                                 (0: FD_DEFAULT_ODD_XCD_PERMILLE; -1: equal splits) */
+  int32_t odd_xcd_permille;   /* MI355X rule, 256 CUs, against the odd XCDs' slower streaming (the
+                                 hardware places workgroup w on XCD w mod 8). Uniform plans it makes
+                                 (not forced), contiguous cache, even split count: odd-numbered
+                                 splits get 1000 - x tokens per 1000 of an even split's 1000 + x.
+                                 Balanced plans with a multiple of 8 ranges averaging at least
+                                 FD_XCD_SHIFT_MIN_RANGE_TOKENS, where every odd range keeps at
+                                 least one granule: odd ranges get the smaller parts
+                                 (fd_plan_t::odd_range_permille). 0: FD_DEFAULT_ODD_XCD_PERMILLE;
+                                 -1: equal splits and ranges */
   int32_t reserved[3];
   /* Optional HOST copy of seq_lens (int32 [batch]). With it the MI355X rule
    * sizes splits from the batch's total work: no split longer than one
@@ -243,6 +257,9 @@ typedef struct {
   int32_t piece_cost;         /* BALANCED: granules of start-up cost added per non-empty segment */
   int32_t odd_chunk_tokens;   /* UNIFORM: tokens of an odd-numbered split; chunk_tokens is an
                                  even-numbered split's (equal unless odd_xcd_permille shifted them) */
+  int32_t odd_range_permille; /* BALANCED: x in 0..999, the alternating range sizes (fd_schedule);
+                                 0: N equal ranges. UNIFORM: 0 */
+  int32_t reserved3;
   int64_t ws_o_bytes;         /* float [B, Hq, S, D] */
   int64_t ws_stats_bytes;     /* float [B, Hq, S, 2] (UML: m, l) or [B, Hq, S] (OLSE: lse) */
   int64_t ws_counter_bytes;   /* uint32 [B, Hkv] arrival counters of fd_decode_fused */
@@ -356,7 +373,8 @@ FD_API int fd_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t s
  * split-kernel launch of at most FD_WG_STAMP_RECORDS workgroups, four uint64
  * per workgroup w (linear index over the grid x, y, z): its start and end on
  * the device's 100 MHz constant clock, the K/V tokens it streamed, and its
- * piece count | its XCD id << 32. fd_wg_stamps copies the records of the
+ * piece count | its XCD id << 32 | its CU's place in the XCD << 40 (bits 8..15
+ * of the hardware id register: CU, shader array, shader engine). fd_wg_stamps copies the records of the
  * current device (the last launch's, for the workgroups it had) into device
  * memory dst (dst_bytes, at most FD_WG_STAMP_RECORDS * 32 bytes are copied)
  * on stream. Other builds record nothing and return FD_ERR_UNSUPPORTED. */

@@ -112,13 +112,18 @@ def chunk_from_lengths(lengths, max_len: int, kv_heads: int, slots: int, align: 
         chunk += align
 
 
-def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_granules: int = 4, cost: int = 0):
+def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_granules: int = 4, cost: int = 0,
+                      odd_permille: int = 0):
     """The balanced split schedule, from its definition: segment (b, h) is
     cdiv(len_b, G) token granules followed by ``cost`` granules that hold no
     tokens (a piece's start-up cost; none for an empty segment); the
     segments, in (b, h) order, form one line of T granules; N = min(slots,
     cdiv(T, min_granules)) workgroups (1 if T = 0) take the ranges
-    [floor(w T / N), floor((w + 1) T / N)). Every non-empty intersection of a
+    [floor(w T / N), floor((w + 1) T / N)); with ``odd_permille`` = x > 0
+    range w instead holds 1000 + x parts (w even) or 1000 - x parts (w odd),
+    its start being floor(T * (parts of ranges before w) / (all parts)), so
+    that odd workgroups, which the hardware places on the slower odd XCDs,
+    get less of the line. Every non-empty intersection of a
     range with a segment's token granules is one piece. Returns (N, S,
     pieces, T) with pieces[(b, h)] = [(w, token_lo, token_hi), ...] in
     workgroup order and S = the largest number of pieces of one segment (at
@@ -131,7 +136,10 @@ def balanced_schedule(lengths, kv_heads: int, granule: int, slots: int, min_gran
     seg = [p + cost if p > 0 else 0 for p in plens]
     T = kv_heads * sum(seg)
     N = min(slots, cdiv(T, min_granules)) if T > 0 else 1
-    ranges = [(w * T // N, (w + 1) * T // N) for w in range(N)]
+    parts = [1000 + odd_permille if w % 2 == 0 else 1000 - odd_permille for w in range(N)]
+    before = [sum(parts[:w]) for w in range(N + 1)]
+    cuts = [T * c // before[N] for c in before]
+    ranges = list(zip(cuts[:-1], cuts[1:]))
     pieces = {}
     x = 0
     for b, (n, plen, sl) in enumerate(zip(lens, plens, seg)):

@@ -106,6 +106,7 @@ int main(int argc, char** argv) {
       o.overhead_budget = rng() % 4 == 0 ? (float)(rng() % 2000) * 1e-3f : 0.0f;
       o.schedule = rng() % 3;
       o.piece_cost_tokens = rng() % 3 == 0 ? -1 : (rng() % 3 == 0 ? (int32_t)(rng() % 4096) : 0);
+      o.odd_xcd_permille = rng() % 4 == 0 ? (int32_t)(rng() % 1001) - 1 : 0;
       if (o.host_seq_lens) o.num_host_seq_lens = p.batch;
     }
     fd_plan_t pl;
@@ -119,6 +120,22 @@ int main(int argc, char** argv) {
       // uniform split s starts at token s * chunk, a 32-bit index on the device
       if (pl.schedule == FD_SCHEDULE_UNIFORM && (int64_t)pl.num_splits * pl.chunk_tokens > INT32_MAX) {
         printf("iter %ld: split boundaries overflow: S=%d chunk=%d\n", it, pl.num_splits, pl.chunk_tokens);
+        return 1;
+      }
+      // weighted balanced cuts multiply granule positions by up to 1000 (N + 2)
+      if (pl.schedule == FD_SCHEDULE_BALANCED && pl.odd_range_permille > 0) {
+        const fd_problem& q = pl.prob;
+        const int64_t cap = q.layout == FD_LAYOUT_PAGED ? (int64_t)q.max_pages_per_seq * q.page_size : q.kv_capacity;
+        const int64_t G = pl.chunk_tokens;
+        const int64_t t_max = (int64_t)q.batch * q.num_kv_heads * ((cap + G - 1) / G + pl.piece_cost);
+        if ((__int128)t_max * (1000 * ((__int128)pl.grid_x + 2)) > ((__int128)1 << 62)) {
+          printf("iter %ld: weighted cut overflows: t_max=%ld N=%d\n", it, (long)t_max, pl.grid_x);
+          return 1;
+        }
+      }
+      if (pl.odd_range_permille < 0 || pl.odd_range_permille > 999 ||
+          (pl.schedule != FD_SCHEDULE_BALANCED && pl.odd_range_permille != 0)) {
+        printf("iter %ld: bad odd_range_permille %d\n", it, pl.odd_range_permille);
         return 1;
       }
     } else ++bad;

@@ -208,10 +208,49 @@ def test_balanced_schedule_matches_oracle(paged):
         G = max(32, page)
         assert plan.slots == cus                       # one range per CU by default
         assert plan.piece_cost == -(-512 // G)           # default start-up cost: 512 tokens
-        N, S, _, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots, cost=plan.piece_cost)
+        N, S, _, _ = OP.balanced_schedule(lens, Hkv, G, plan.slots, cost=plan.piece_cost,
+                                          odd_permille=plan.odd_range_permille)
         assert (plan.grid_x, plan.grid_y, plan.grid_z) == (N, 1, 1), (lens, cus)
         assert plan.num_splits == S and plan.chunk_tokens == G
         assert plan.ws_o_bytes == B * Hkv * g * S * 128 * 4
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_odd_ranges_match_oracle(paged):
+    """Ranges of alternating size: the planner turns them on exactly when the
+    MI355X rule runs on 256 CUs with a multiple of 8 ranges averaging at least
+    FD_XCD_SHIFT_MIN_RANGE_TOKENS of K/V rows and every odd range keeps a
+    granule, with the default 45 per mille or the caller's x; its split count
+    S then equals the oracle's for the same alternating cut."""
+    rng = np.random.default_rng(31)
+    seen = set()
+    for trial in range(120):
+        B = int(rng.choice([3, 8, 16, 64]))
+        Hkv, g = ((8, 4), (2, 2), (4, 1), (8, 8))[trial % 4]
+        lens = [int(n) if rng.random() > 0.1 else 0 for n in rng.integers(0, int(rng.choice([3000, 60000])), B)]
+        L = max(lens + [1])
+        x = int(rng.choice([0, 1, 45, 250, 999]))
+        wpc = int(rng.choice([1, 2]))
+        mk = paged_problem if paged else contiguous_problem
+        page = int(rng.choice([16, 64])) if paged else 0
+        prob = mk(B=B, Hq=Hkv * g, Hkv=Hkv, L=L, **({"page": page} if paged else {}))
+        plan = fd.fd_plan(prob, num_cus=256, wgs_per_cu=wpc, host_seq_lens=lens, schedule="balanced",
+                          odd_xcd_permille=x)
+        N = plan.grid_x
+        T = OP.balanced_schedule(lens, Hkv, plan.chunk_tokens, plan.slots, cost=plan.piece_cost)[3]
+        on = N % 8 == 0 and Hkv * sum(lens) >= 4096 * N and (1000 - (x or 45)) * T >= 1000 * N
+        assert plan.odd_range_permille == ((x or 45) if on else 0), (lens, x, N)
+        seen.add((on, x))
+        N2, S, _, _ = OP.balanced_schedule(lens, Hkv, plan.chunk_tokens, plan.slots, cost=plan.piece_cost,
+                                           odd_permille=plan.odd_range_permille)
+        assert (N, plan.num_splits) == (N2, S), (lens, x)
+        off = fd.fd_plan(prob, num_cus=256, wgs_per_cu=wpc, host_seq_lens=lens, schedule="balanced",
+                         odd_xcd_permille=-1)
+        assert off.odd_range_permille == 0 and off.grid_x == N
+        assert fd.fd_plan(prob, num_cus=255, host_seq_lens=lens, schedule="balanced").odd_range_permille == 0
+        assert fd.fd_plan(prob, num_cus=256, host_seq_lens=lens, schedule="balanced",
+                          heuristic="fa2").odd_range_permille == 0
+    assert {on for on, _ in seen} == {False, True} and (True, 250) in seen
 
 
 def test_schedule_selection():

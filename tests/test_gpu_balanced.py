@@ -43,6 +43,12 @@ def case(name):
     if name == "f32_g2":                         # VALU kernel, fp32 cache, g = 2
         return W.contiguous(name, seed=101, batch=3, q_heads=8, kv_heads=4, head_dim=64, capacity=1500,
                             seq_lens=[1500, 40, 700], dtype="f32")
+    if name == "gqa8_f16_long_ragged":           # over 4096 K/V rows per range on 256 CUs: alternating ranges
+        return W.contiguous(name, seed=103, batch=8, q_heads=32, kv_heads=8, head_dim=128, capacity=40000,
+                            seq_lens=[30000, 5000, 20000, 1, 40000, 12000, 25000, 0], dtype="f16")
+    if name == "paged_long_ragged":
+        return W.paged(name, seed=104, batch=6, q_heads=32, kv_heads=8, head_dim=128,
+                       seq_lens=[40000, 900, 33000, 0, 29000, 30000], page_size=16, dtype="f16")
     if name == "paged_mha":
         return W.paged(name, seed=102, batch=4, q_heads=8, kv_heads=8, head_dim=128,
                        seq_lens=[3000, 16, 0, 1700], page_size=32, dtype="f16")
@@ -68,16 +74,21 @@ def test_balanced_matches_oracle(name, cus):
 
 
 @pytest.mark.parametrize("ws_format", ["uml", "olse"])
-@pytest.mark.parametrize("name", ["gqa8_f16_ragged", "paged_16_hnd", "mha_f16_ragged"])
-def test_balanced_partial_states(name, ws_format):
+@pytest.mark.parametrize("name,cus", [("gqa8_f16_ragged", 7), ("paged_16_hnd", 7), ("mha_f16_ragged", 7),
+                                      ("gqa8_f16_long_ragged", 256), ("paged_long_ragged", 256)])
+def test_balanced_partial_states(name, cus, ws_format):
     """Slot i of segment (b, h) holds the state of its i-th piece; slots past
-    the segment's piece count hold the neutral state."""
+    the segment's piece count hold the neutral state. On 256 CUs the long
+    batches get ranges of alternating size (odd ranges smaller), and the
+    pieces are those of the oracle's alternating cut."""
     w = case(name)
-    cus = 7
     plan, out, lse, ws_o, ws_stats = H.run(w, num_cus=cus, ws_format=ws_format, schedule="balanced")
     assert plan.schedule == BAL
+    assert plan.odd_range_permille == (45 if cus == 256 else 0)
+    H.say(f"{name}: N={plan.grid_x} S={plan.num_splits} odd_range_permille={plan.odd_range_permille}")
     lens = w.seq_lens.tolist()
-    N, S, pieces, _ = OP.balanced_schedule(lens, w.num_kv_heads, plan.chunk_tokens, plan.slots, cost=plan.piece_cost)
+    N, S, pieces, _ = OP.balanced_schedule(lens, w.num_kv_heads, plan.chunk_tokens, plan.slots, cost=plan.piece_cost,
+                                           odd_permille=plan.odd_range_permille)
     assert (plan.grid_x, plan.num_splits) == (N, S)
     B, Hq = w.batch, w.num_q_heads
     M, Lw, U = A.split_states(H.cache_of(w), S, plan.chunk_tokens,
@@ -99,7 +110,7 @@ def test_balanced_partial_states(name, ws_format):
 
 @pytest.mark.parametrize("cus", [256, 5])
 @pytest.mark.parametrize("name", ["gqa8_f16_ragged", "gqa2_f16_many_tiny", "all_empty", "paged_16_hnd",
-                                  "mha_f16_ragged", "f32_g2"])
+                                  "mha_f16_ragged", "f32_g2", "gqa8_f16_long_ragged", "paged_long_ragged"])
 def test_balanced_fused(name, cus):
     w = case(name)
     plan, out, lse, ctr = H.run_fused(w, num_cus=cus, schedule="balanced")

@@ -154,6 +154,73 @@ def test_balanced_schedule_worked_example():
     }
 
 
+def test_balanced_schedule_odd_ranges_worked_example():
+    """The same line of T = 10 granules (segments at [0,3), [3,6), [6,8),
+    [8,10)) cut into four ranges of alternating size, x = 500: parts 1500,
+    500, 1500, 500 of 4000, so the ranges start at floor(10 * c / 4000) for
+    c = 0, 1500, 2000, 3500: granules 0, 3, 5, 8, i.e. [0,3), [3,5), [5,8),
+    [8,10). Segment (0,1) is cut after its second granule (token 64)."""
+    N, S, pieces, T = P.balanced_schedule([96, 40], 2, 32, 4, min_granules=1, odd_permille=500)
+    assert (N, S, T) == (4, 2, 10)
+    assert pieces == {
+        (0, 0): [(0, 0, 96)],
+        (0, 1): [(1, 0, 64), (2, 64, 96)],
+        (1, 0): [(2, 0, 40)],
+        (1, 1): [(3, 0, 40)],
+    }
+    assert P.balanced_schedule([96, 40], 2, 32, 4, min_granules=1, odd_permille=0) == \
+        P.balanced_schedule([96, 40], 2, 32, 4, min_granules=1)
+
+
+def test_balanced_schedule_odd_ranges_shares():
+    """With alternating range sizes every range holds its exact share of the
+    line, T (1000 +- x) / (1000 N) granules, to within one granule; pieces
+    still tile every segment in order; and x = 0 gives the equal cut."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for trial in range(150):
+        B = int(rng.integers(1, 16))
+        hkv, G, cost = int(rng.choice([1, 2, 8])), int(rng.choice([16, 32])), int(rng.choice([0, 2, 16]))
+        x = int(rng.choice([0, 1, 45, 300, 999]))
+        lens = [int(n) if rng.random() > 0.2 else 0 for n in rng.integers(0, int(rng.choice([300, 5000])), B)]
+        slots = int(rng.choice([2, 8, 64, 256]))
+        N, S, pieces, T = P.balanced_schedule(lens, hkv, G, slots, cost=cost, odd_permille=x)
+        parts = [1000 + x if w % 2 == 0 else 1000 - x for w in range(N)]
+        tokens_of = [0] * N
+        for (b, h), lst in pieces.items():
+            n = lens[b]
+            if n == 0:
+                assert lst == []
+                continue
+            assert lst[0][1] == 0 and lst[-1][2] == n and len(lst) <= S
+            for (w0, _, hi0), (w1, lo1, _) in zip(lst, lst[1:]):
+                assert hi0 == lo1 and w1 > w0 and lo1 % G == 0
+            for w, lo, hi in lst:
+                tokens_of[w] += -(-hi // G) - lo // G
+        if T == 0:
+            continue
+        # a range's token granules plus the cost granules it covers; recount the latter from the line
+        seg = [(-(-n // G) + cost) if n > 0 else 0 for n in lens]
+        line = []
+        for b in range(B):
+            for h in range(hkv):
+                line += [1] * (-(-lens[b] // G)) + [0] * (cost if lens[b] > 0 else 0)
+        assert len(line) == T == hkv * sum(seg)
+        share = []
+        pos = 0
+        M = sum(parts)
+        for w in range(N):
+            exact = T * parts[w] / M
+            end = (T * sum(parts[:w + 1])) // M
+            share.append(end - pos)
+            assert sum(line[pos:end]) == tokens_of[w]
+            assert abs(share[-1] - exact) < 1 + 1e-9
+            pos = end
+        assert pos == T
+        if x == 0:
+            assert P.balanced_schedule(lens, hkv, G, slots, cost=cost) == (N, S, pieces, T)
+
+
 def test_length_aware_chunk_worked_example():
     """By hand: lengths [1000, 3000] over 8 KV heads are 32 000 token-heads of
     work; one slot's share on 256 slots is cdiv(32000, 256) = 125 tokens,
