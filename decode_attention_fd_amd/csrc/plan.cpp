@@ -384,9 +384,12 @@ int plan_core(const fd_problem* prob, const fd_plan_opts* o, int balanced_wgs_pe
     // the even ones, launch after launch (while which half of the chip is
     // slowest changes from one launch to the next). Odd-numbered splits give
     // odd_xcd_permille of their tokens to the even-numbered ones; the splits
-    // still cover S * chunk tokens.
+    // still cover S * chunk tokens. Only splits long enough to be bound by
+    // streaming: at 64/8 GQA the split kernel gained 0.3-1.1 us at 2000-token
+    // splits (64k tokens), 1.5-2.6 us at 4000-8192, and lost 0.5 us at 1000 and
+    // 1.0-1.4 us at 500 (32k, 16k tokens).
     if (o->heuristic == FD_HEURISTIC_MI355X && !paged && S % 2 == 0 && o->num_cus == 256 &&
-        o->odd_xcd_permille >= 0) {
+        o->odd_xcd_permille >= 0 && chunk >= FD_XCD_SHIFT_MIN_SPLIT_TOKENS) {
       const int64_t x = o->odd_xcd_permille > 0 ? o->odd_xcd_permille : FD_DEFAULT_ODD_XCD_PERMILLE;
       const int64_t shift = chunk * x / 1000;
       if (shift > 0 && shift < chunk) {

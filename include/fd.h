@@ -150,6 +150,11 @@ typedef enum {
  * (fd_plan_opts::odd_xcd_permille). */
 #define FD_DEFAULT_ODD_XCD_PERMILLE 45
 
+/* Uniform plans shift tokens from odd-numbered splits only when a split
+ * holds at least this many tokens: shorter splits are bound by their fixed
+ * start-up and epilogue costs, where the shift only lengthens the even ones. */
+#define FD_XCD_SHIFT_MIN_SPLIT_TOKENS 1536
+
 /* The balanced schedule shifts work from odd-XCD ranges only when a range
  * averages at least this many tokens of K/V rows (KV heads x tokens / N):
  * shorter ranges are bound by their pieces' start-up latencies, not by the
@@ -218,8 +223,9 @@ typedef struct {
                                  (0: FD_DEFAULT_PIECE_COST_TOKENS; -1: none) */
   int32_t odd_xcd_permille;   /* MI355X rule, 256 CUs, against the odd XCDs' slower streaming (the
                                  hardware places workgroup w on XCD w mod 8). Uniform plans it makes
-                                 (not forced), contiguous cache, even split count: odd-numbered
-                                 splits get 1000 - x tokens per 1000 of an even split's 1000 + x.
+                                 (not forced), contiguous cache, even split count, splits of at
+                                 least FD_XCD_SHIFT_MIN_SPLIT_TOKENS: odd-numbered splits get
+                                 1000 - x tokens per 1000 of an even split's 1000 + x.
                                  Balanced plans with a multiple of 8 ranges averaging at least
                                  FD_XCD_SHIFT_MIN_RANGE_TOKENS, where every odd range keeps at
                                  least one granule: odd ranges get the smaller parts

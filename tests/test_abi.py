@@ -98,14 +98,15 @@ def test_fa2_heuristic_reproduces_page_table():
 
 def base_chunk(plan, paged=False, cus=256):
     """The split rule's chunk of a uniform plan, after checking the odd-XCD
-    shift: with an even split count on a 256-CU device (contiguous cache),
-    even-numbered splits hold chunk + shift and odd ones chunk - shift tokens,
-    shift = chunk * FD_DEFAULT_ODD_XCD_PERMILLE // 1000; else both chunk."""
+    shift: with an even split count on a 256-CU device (contiguous cache) and
+    splits of at least FD_XCD_SHIFT_MIN_SPLIT_TOKENS (1536), even-numbered
+    splits hold chunk + shift and odd ones chunk - shift tokens, shift =
+    chunk * FD_DEFAULT_ODD_XCD_PERMILLE // 1000; else both chunk."""
     c, c_odd, S = plan.chunk_tokens, plan.odd_chunk_tokens, plan.num_splits
     assert (c + c_odd) % 2 == 0
     base = (c + c_odd) // 2
     shift = base * 45 // 1000
-    if not paged and S % 2 == 0 and cus == 256 and 0 < shift < base:
+    if not paged and S % 2 == 0 and cus == 256 and base >= 1536 and 0 < shift < base:
         assert (c, c_odd) == (base + shift, base - shift), (S, c, c_odd)
     else:
         assert c == c_odd, (S, c, c_odd)
@@ -147,6 +148,11 @@ def test_mi355x_choices_for_the_workloads():
     assert p.chunk_tokens == p.odd_chunk_tokens                      # not the 256-CU device
     p = fd.fd_plan(contiguous_problem(Hq=64, Hkv=8, L=128000), num_cus=256, force_splits=32)
     assert p.chunk_tokens == p.odd_chunk_tokens == 4000               # forced plans keep equal splits
+    for L, chunk in ((16000, 500), (32000, 1000), (48000, 1500)):  # short splits stay equal
+        p = fd.fd_plan(contiguous_problem(B=1, Hq=64, Hkv=8, L=L), num_cus=256)
+        assert (p.num_splits, p.chunk_tokens, p.odd_chunk_tokens) == (32, chunk, chunk), L
+    p = fd.fd_plan(contiguous_problem(B=1, Hq=64, Hkv=8, L=64000), num_cus=256)
+    assert (p.chunk_tokens, p.odd_chunk_tokens) == (2090, 1910)
     assert _status(contiguous_problem(), odd_xcd_permille=1000) == fd.FD_ERR_INVALID_ARG
     assert _status(contiguous_problem(), odd_xcd_permille=-2) == fd.FD_ERR_INVALID_ARG
     assert fd.fd_plan(contiguous_problem(B=64, Hq=32, Hkv=8, L=2048), num_cus=256).num_splits == 1

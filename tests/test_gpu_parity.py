@@ -48,11 +48,12 @@ def test_tiny_partial_states_match_oracle_splits(fmt):
 @pytest.mark.parametrize("fmt", ["uml", "olse"])
 def test_odd_xcd_shifted_plan_states(fmt):
     """A uniform plan the MI355X rule shifts (even split count, contiguous cache,
-    256 CUs): even-numbered splits hold chunk_tokens tokens and odd-numbered
-    ones odd_chunk_tokens. Every split state of sampled rows against the
-    oracle's states over the same alternating partition, and every output."""
-    w = W.contiguous("xcd_shift", seed=120, batch=2, q_heads=64, kv_heads=8, head_dim=128, capacity=20000,
-                     seq_lens=[20000, 13001], dtype="f16")
+    256 CUs, splits of at least 1536 tokens; here S = 20 of 2547 / 2329):
+    even-numbered splits hold chunk_tokens tokens and odd-numbered ones
+    odd_chunk_tokens. Every split state of sampled rows against the oracle's
+    states over the same alternating partition, and every output."""
+    w = W.contiguous("xcd_shift", seed=120, batch=2, q_heads=64, kv_heads=8, head_dim=128, capacity=48000,
+                     seq_lens=[48000, 30001], dtype="f16")
     plan, out, lse, ws_o, ws_stats = H.run(w, ws_format=fmt, schedule="uniform")
     H.say(f"shifted plan: S={plan.num_splits} chunks {plan.chunk_tokens}/{plan.odd_chunk_tokens}")
     assert plan.num_splits % 2 == 0 and plan.chunk_tokens > plan.odd_chunk_tokens
