@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitParams p) {
   // odd-numbered splits of chunk and chunk_odd tokens; formed in 64 bits (the
   // plan bounds the splits' end by INT32_MAX, but a start past the sequence
   // must never wrap to a negative token index).
-  const int64_t s0 = (int64_t)(s >> 1) * (p.chunk + p.chunk_odd) + ((s & 1) ? p.chunk : 0);
+  const int64_t s0 = (int64_t)(s >> 1) * ((int64_t)p.chunk + p.chunk_odd) + ((s & 1) ? p.chunk : 0);
   const int64_t len = (s & 1) ? p.chunk_odd : p.chunk;
   const int start = (int)(s0 < seq_len ? s0 : seq_len);
   const int end = (int)(s0 + len < seq_len ? s0 + len : seq_len);
