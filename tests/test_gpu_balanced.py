@@ -46,6 +46,12 @@ def case(name):
     if name == "gqa8_f16_long_ragged":           # over 4096 K/V rows per range on 256 CUs: alternating ranges
         return W.contiguous(name, seed=103, batch=8, q_heads=32, kv_heads=8, head_dim=128, capacity=40000,
                             seq_lens=[30000, 5000, 20000, 1, 40000, 12000, 25000, 0], dtype="f16")
+    if name == "mha_f16_long_ragged":            # VALU kernel with alternating ranges on 256 CUs
+        return W.contiguous(name, seed=105, batch=4, q_heads=8, kv_heads=8, head_dim=128, capacity=50000,
+                            seq_lens=[40000, 30000, 50000, 20001], dtype="f16")
+    if name == "gqa4_bf16_long_qblock2":         # two-row query block with alternating ranges on 256 CUs
+        return W.contiguous(name, seed=106, batch=4, q_heads=32, kv_heads=8, head_dim=128, capacity=50000,
+                            seq_lens=[50000, 33, 45000, 41000], dtype="bf16", q_len=2)
     if name == "paged_long_ragged":
         return W.paged(name, seed=104, batch=6, q_heads=32, kv_heads=8, head_dim=128,
                        seq_lens=[40000, 900, 33000, 0, 29000, 30000], page_size=16, dtype="f16")
@@ -60,8 +66,12 @@ def case(name):
     raise KeyError(name)
 
 
+# batches with over 4096 K/V rows per range on 256 CUs: ranges of alternating size there
+ALTERNATING = {"gqa8_f16_long_ragged", "paged_long_ragged", "mha_f16_long_ragged", "gqa4_bf16_long_qblock2"}
+
 CASES = ["gqa8_f16_ragged", "gqa4_bf16_d64", "gqa2_f16_many_tiny", "all_empty", "one_long",
-         "paged_16_hnd", "paged_64_nhd", "mha_f16_ragged", "mha_bf16_d64_qblock", "f32_g2", "paged_mha"]
+         "paged_16_hnd", "paged_64_nhd", "mha_f16_ragged", "mha_bf16_d64_qblock", "f32_g2", "paged_mha",
+         "mha_f16_long_ragged", "gqa4_bf16_long_qblock2"]
 
 
 @pytest.mark.parametrize("cus", [256, 5])
@@ -70,6 +80,8 @@ def test_balanced_matches_oracle(name, cus):
     w = case(name)
     plan, out, lse, ws_o, ws_stats = H.run(w, num_cus=cus, schedule="balanced")
     assert plan.schedule == BAL
+    if name in ALTERNATING:                     # alternating ranges on 256 CUs only
+        assert plan.odd_range_permille == (45 if cus == 256 else 0)
     H.check_against_oracle(w, out, lse)
 
 
@@ -110,7 +122,8 @@ def test_balanced_partial_states(name, cus, ws_format):
 
 @pytest.mark.parametrize("cus", [256, 5])
 @pytest.mark.parametrize("name", ["gqa8_f16_ragged", "gqa2_f16_many_tiny", "all_empty", "paged_16_hnd",
-                                  "mha_f16_ragged", "f32_g2", "gqa8_f16_long_ragged", "paged_long_ragged"])
+                                  "mha_f16_ragged", "f32_g2", "gqa8_f16_long_ragged", "paged_long_ragged",
+                                  "mha_f16_long_ragged", "gqa4_bf16_long_qblock2"])
 def test_balanced_fused(name, cus):
     w = case(name)
     plan, out, lse, ctr = H.run_fused(w, num_cus=cus, schedule="balanced")

@@ -73,6 +73,37 @@ def test_odd_xcd_shifted_plan_states(fmt):
             assert abs(lse_s[b, h, s] - lse_ref) < 1e-5 * max(1, abs(lse_ref)), (b, h, s)
 
 
+SHIFTED_CASES = {
+    # name: (workload arguments, odd_xcd_permille, fused)
+    "mha_bf16_valu": (dict(batch=1, q_heads=8, kv_heads=8, head_dim=128, capacity=50000, seq_lens=[50000],
+                           dtype="bf16"), 0, False),
+    "gqa4_f16_d64_qblock2": (dict(batch=2, q_heads=16, kv_heads=4, head_dim=64, capacity=60000,
+                                  seq_lens=[60000, 41000], dtype="f16", q_len=2), 300, False),
+    "gqa2_f32_d64_valu": (dict(batch=1, q_heads=8, kv_heads=4, head_dim=64, capacity=120000, seq_lens=[120000],
+                               dtype="f32"), 100, False),
+    "gqa8_bf16_fused": (dict(batch=1, q_heads=64, kv_heads=8, head_dim=128, capacity=50000, seq_lens=[50000],
+                             dtype="bf16"), 0, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHIFTED_CASES))
+def test_odd_xcd_shifted_plan_variants(name):
+    """Shifted uniform plans on both kernels (VALU for g = 1 and fp32 caches),
+    a two-row query block, a large shift (300 per mille) and the fused call:
+    every output row against the oracle."""
+    kw, x, fused = SHIFTED_CASES[name]
+    w = W.contiguous(name, seed=130, **kw)
+    opts = dict(num_cus=256, schedule="uniform", odd_xcd_permille=x)
+    if fused:
+        plan, out, lse, ctr = H.run_fused(w, **opts)
+        assert torch.all(ctr == 0).item()
+    else:
+        plan, out, lse, _, _ = H.run(w, **opts)
+    H.say(f"{name}: S={plan.num_splits} chunks {plan.chunk_tokens}/{plan.odd_chunk_tokens} kernel={plan.kernel}")
+    assert plan.num_splits % 2 == 0 and plan.chunk_tokens > plan.odd_chunk_tokens
+    H.check_against_oracle(w, out, lse)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("q_gain", [1.0, 40.0])
 def test_ragged_batch_with_empty_splits(splits, q_gain):
