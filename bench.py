@@ -83,14 +83,14 @@ def plan_options(w, splits: int = 0, schedule: str = "auto", wgs_per_cu: int = 0
 
 
 def choose_path(plan, path: str = "auto") -> str:
-    """auto: the fused call when the plan has one split (its rows are written
-    directly) or is balanced (its one-piece segments are written directly and
-    only the others are merged), else split + merge."""
+    """auto: the library's choice (decode_attention_fd_amd.prefers_fused): the
+    fused call when the plan has one split or is balanced with at least 4096
+    output rows, else split + merge."""
     import decode_attention_fd_amd as fd
 
     if path != "auto":
         return path
-    return "fused" if plan.num_splits == 1 or plan.schedule == fd.SCHEDULES["balanced"] else "split"
+    return "fused" if fd.prefers_fused(plan) else "split"
 
 
 def kernel_source_hash(kernel: str = "mfma") -> str:

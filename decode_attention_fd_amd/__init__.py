@@ -432,17 +432,35 @@ def fd_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _check(st, "fd_read_probe")
 
 
+# Output rows (B * q_len * Hq) from which a balanced plan is faster as one fused
+# launch than as split + merge on MI355X. Twelve ragged batches (lengths
+# U[1, hi], 32 or 64 query heads over 8 or 32 KV heads): at 256-2048 rows split +
+# merge was 0.3-6 us faster (B=4 up to 64k tokens: 64.0 vs 70.1 us), at 4096 and
+# 8192 rows the fused call was (B=128: 101.5 vs 102.9 us; B=256: 180-186 vs
+# 189-194 us), where most segments are one piece written directly and a merge
+# kernel over that many rows costs more than the merges done inside.
+FUSED_MIN_ROWS = 4096
+
+
+def prefers_fused(plan: Plan) -> bool:
+    """Whether one fused launch is the faster path for this plan: one split
+    (its rows are written directly), or a balanced plan of at least
+    FUSED_MIN_ROWS output rows; otherwise split + merge."""
+    rows = plan.prob.batch * max(1, plan.prob.q_len) * plan.prob.num_q_heads
+    return plan.num_splits == 1 or (plan.schedule == SCHEDULES["balanced"] and rows >= FUSED_MIN_ROWS)
+
+
 def flash_decode(q, k, v, seq_lens, block_table=None, *, max_seq_len=None, scale: float = 0.0,
                  return_lse: bool = True, fused: Optional[bool] = None, stream=None, **plan_options):
     """Plan, split and merge (two launches, or one with ``fused=True``; by
-    default one when the plan has a single split, whose rows the split kernel
-    then writes directly); returns (out, lse) fp32 (lse None if not asked)."""
+    default the faster of the two for the plan, ``prefers_fused``); returns
+    (out, lse) fp32 (lse None if not asked)."""
     plan = fd_plan(problem_for(q, k, v, seq_lens, block_table, max_seq_len, scale), **plan_options)
     ws_o, ws_stats = workspace(plan, q.device)
     out = torch.empty(*q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(*q.shape[:-1], dtype=torch.float32, device=q.device) if return_lse else None
     if fused is None:
-        fused = plan.num_splits == 1
+        fused = prefers_fused(plan)
     if fused:
         fd_decode_fused(plan, q, k, v, seq_lens, ws_o, ws_stats, counters(plan, q.device), out, lse, block_table,
                         stream)

@@ -259,6 +259,22 @@ def test_balanced_odd_ranges_match_oracle(paged):
     assert {on for on, _ in seen} == {False, True} and (True, 250) in seen
 
 
+def test_prefers_fused_rule():
+    """The default path: one launch for one split, or for a balanced plan of at
+    least FUSED_MIN_ROWS output rows (B * q_len * Hq); split + merge otherwise."""
+    one = fd.fd_plan(contiguous_problem(B=64, Hq=32, Hkv=8, L=2048), num_cus=256)
+    assert one.num_splits == 1 and fd.prefers_fused(one)
+    uni = fd.fd_plan(contiguous_problem(B=1, Hq=64, Hkv=8, L=128000), num_cus=256)
+    assert uni.num_splits == 32 and not fd.prefers_fused(uni)
+    for B, fused in ((64, False), (127, False), (128, True), (256, True)):    # 32 query heads: rows = 32 B
+        lens = [1 + (37 * i) % 2048 for i in range(B)]
+        p = fd.fd_plan(contiguous_problem(B=B, Hq=32, Hkv=8, L=2048), num_cus=256, host_seq_lens=lens,
+                       schedule="balanced")
+        assert p.schedule == fd.SCHEDULES["balanced"] and p.num_splits > 1, B
+        assert fd.prefers_fused(p) == fused, B
+    assert fd.FUSED_MIN_ROWS == 4096
+
+
 def test_schedule_selection():
     lens = [30000, 10, 0]                        # 8 * 30010 / 256 = 937 tokens per range
     prob = contiguous_problem(B=3, Hq=32, Hkv=8, L=30000)
