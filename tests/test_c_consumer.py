@@ -44,9 +44,9 @@ static void show(const char* tag, int st, const fd_plan_t* pl) {
     printf("%s status %d %s\n", tag, st, fd_status_str(st));
     return;
   }
-  printf("%s status 0 S %d chunk %d kernel %d schedule %d grid %d %d %d ws %lld %lld\n", tag, pl->num_splits,
-         pl->chunk_tokens, pl->kernel, pl->schedule, pl->grid_x, pl->grid_y, pl->grid_z,
-         (long long)pl->ws_o_bytes, (long long)pl->ws_stats_bytes);
+  printf("%s status 0 S %d chunk %d/%d kernel %d schedule %d grid %d %d %d odd %d ws %lld %lld\n", tag,
+         pl->num_splits, pl->chunk_tokens, pl->odd_chunk_tokens, pl->kernel, pl->schedule, pl->grid_x, pl->grid_y,
+         pl->grid_z, pl->odd_range_permille, (long long)pl->ws_o_bytes, (long long)pl->ws_stats_bytes);
 }
 
 int main(void) {
@@ -54,6 +54,7 @@ int main(void) {
   fd_plan_opts o;
   fd_plan_t pl;
   int32_t lens[6] = {3000, 17, 0, 2200, 5000, 900};
+  int32_t long_lens[8] = {40000, 30000, 35000, 20000, 38000, 25000, 39000, 31000};
 
   printf("version %s\n", fd_version());
   printf("sizes %zu %zu %zu %zu\n", sizeof(fd_problem), sizeof(fd_plan_opts), sizeof(fd_plan_t), sizeof(fd_args));
@@ -71,6 +72,14 @@ int main(void) {
   o.host_seq_lens = lens;
   o.num_host_seq_lens = 6;
   show("balanced", fd_plan(&p, &o, &pl), &pl);
+
+  /* over 4096 K/V rows per range on 256 CUs: ranges of alternating size */
+  contiguous(&p, 8, 32, 8, 128, 40000);
+  o.host_seq_lens = long_lens;
+  o.num_host_seq_lens = 8;
+  show("balanced_long", fd_plan(&p, &o, &pl), &pl);
+  o.odd_xcd_permille = -1;
+  show("balanced_long_equal", fd_plan(&p, &o, &pl), &pl);
 
   /* a workspace one float short of the plan's: refused before any launch */
   contiguous(&p, 1, 64, 8, 128, 128000);
@@ -110,8 +119,8 @@ def _python_side() -> list:
             pl = fn()
         except fd.FdError as e:
             return f"{tag} status {e.status} {fd.status_str(e.status)}"
-        return (f"{tag} status 0 S {pl.num_splits} chunk {pl.chunk_tokens} kernel {pl.kernel} "
-                f"schedule {pl.schedule} grid {pl.grid_x} {pl.grid_y} {pl.grid_z} "
+        return (f"{tag} status 0 S {pl.num_splits} chunk {pl.chunk_tokens}/{pl.odd_chunk_tokens} kernel {pl.kernel} "
+                f"schedule {pl.schedule} grid {pl.grid_x} {pl.grid_y} {pl.grid_z} odd {pl.odd_range_permille} "
                 f"ws {pl.ws_o_bytes} {pl.ws_stats_bytes}")
 
     L = fd.lib()
@@ -122,6 +131,11 @@ def _python_side() -> list:
     lines.append(show("balanced", lambda: fd.fd_plan(contiguous(6, 32, 8, 128, 5000), num_cus=256,
                                                      schedule="balanced",
                                                      host_seq_lens=[3000, 17, 0, 2200, 5000, 900])))
+    long_lens = [40000, 30000, 35000, 20000, 38000, 25000, 39000, 31000]
+    for tag, x in (("balanced_long", 0), ("balanced_long_equal", -1)):
+        lines.append(show(tag, lambda x=x: fd.fd_plan(contiguous(8, 32, 8, 128, 40000), num_cus=256,
+                                                      schedule="balanced", host_seq_lens=long_lens,
+                                                      odd_xcd_permille=x)))
     pl = fd.fd_plan(contiguous(1, 64, 8, 128, 128000), num_cus=256)
     st = L.fd_merge(ctypes.byref(pl), 4096, pl.ws_o_bytes - 4, 8192, pl.ws_stats_bytes, 4096, None, None)
     lines.append(f"merge_short status {st} {fd.status_str(st)}")
@@ -140,7 +154,9 @@ def test_plain_c_program_sees_the_same_library(tmp_path):
                     str(src), "-o", str(exe), f"-L{libdir}", "-lfd", f"-Wl,-rpath,{libdir}"], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.strip().splitlines()
     assert out == _python_side()
-    assert out[2].startswith("gqa status 0 ") and out[3].startswith("bad status 1 ")
-    assert " schedule 2 " in out[4]
-    assert out[5] == f"merge_short status {fd.FD_ERR_WORKSPACE} {fd.status_str(fd.FD_ERR_WORKSPACE)}"
-    assert out[6].startswith(f"overflow status {fd.FD_ERR_UNSUPPORTED} ")
+    assert out[2].startswith("gqa status 0 S 32 chunk 4180/3820 ") and out[3].startswith("bad status 1 ")
+    assert " schedule 2 " in out[4] and " odd 0 " in out[4]
+    assert " schedule 2 " in out[5] and " odd 45 " in out[5]          # alternating ranges
+    assert " schedule 2 " in out[6] and " odd 0 " in out[6]           # turned off
+    assert out[7] == f"merge_short status {fd.FD_ERR_WORKSPACE} {fd.status_str(fd.FD_ERR_WORKSPACE)}"
+    assert out[8].startswith(f"overflow status {fd.FD_ERR_UNSUPPORTED} ")
