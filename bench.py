@@ -287,6 +287,46 @@ def wg_stamp_report(plan, launch, launches: int, torch, fd, stream) -> dict:
     return out
 
 
+def trace_follow(trace_dir: str) -> None:
+    """Durations of the kernels in a rocprofv3 kernel trace, keyed by the kernel
+    that ran before each on the same queue: a kernel starts when the one
+    before it ends, so its traced duration includes its own dispatch (what a
+    dependent launch costs). Prints one JSON line."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: (r["Queue_Id"], int(r["Start_Timestamp"])))
+
+    def short(name):
+        for key in ("split_mfma", "split_valu", "merge_kernel", "stream_read_kernel", "elementwise", "copyBuffer"):
+            if key in name:
+                return key
+        return name[:40]
+
+    pairs = {}
+    for a, b in zip(rows, rows[1:]):
+        if a["Queue_Id"] != b["Queue_Id"]:
+            continue
+        key = f"{short(b['Kernel_Name'])} after {short(a['Kernel_Name'])}"
+        pairs.setdefault(key, []).append(((int(b["End_Timestamp"]) - int(b["Start_Timestamp"])) / 1e3,
+                                          (int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3))
+    out = {}
+    for key, v in sorted(pairs.items()):
+        a = np.array(v)
+        out[key] = {"n": len(v), "us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(a[:, 0], [10, 50, 90])],
+                    "gap_us_p50": round(float(np.median(a[:, 1])), 2)}
+    print(json.dumps(out), flush=True)
+
+
 def ctypes_void_p(x):
     import ctypes
 
@@ -472,6 +512,12 @@ def build_parser() -> argparse.ArgumentParser:
     ap.add_argument("--pmc-dump", nargs="+", metavar="DIR",
                     help="print per-kernel counter averages (and kernel-trace durations) of rocprofv3 CSV "
                          "directories, one JSON line per directory and kernel, and exit")
+    ap.add_argument("--launch-floor", type=int, default=0, metavar="ROUNDS",
+                    help="after each split kernel launch, in turn, the merge kernel, two 64-float fills and the "
+                         "read probe over 1 MiB, ROUNDS times each (run under rocprofv3 --kernel-trace; read the "
+                         "trace with --trace-follow)")
+    ap.add_argument("--trace-follow", metavar="DIR",
+                    help="durations of the kernels in a rocprofv3 kernel trace, by the kernel before each")
     ap.add_argument("--pmc-out", default="",
                     help="--pmc-summary: where to write the record (default profiles/traffic_split_<workload>.json; "
                          "'-': print only)")
@@ -488,6 +534,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.workload, *args.pmc_summary, out_path=args.pmc_out)
+        return
+    if args.trace_follow:
+        trace_follow(args.trace_follow)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -553,6 +602,26 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    if args.launch_floor:
+        # after each split kernel, in turn: the merge kernel; two trivial fills
+        # of 64 floats; the read probe over 1 MiB (about the merge's input)
+        small = torch.empty(64, device=dev)
+        pbuf = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        sink = torch.empty(fd.READ_PROBE_SINK_BYTES // 4, dtype=torch.int32, device=dev)
+        for i in range(3 * args.launch_floor):
+            w = ws[i % copies]
+            fd.fd_decode_split(plan, w.q, w.k, w.v, w.seq_lens, ws_o, ws_stats, w.block_table, stream)
+            if i % 3 == 0:
+                fd.fd_merge(plan, ws_o, ws_stats, out, lse, stream)
+            elif i % 3 == 1:
+                small.zero_()
+                small.zero_()
+            else:
+                fd.fd_read_probe(pbuf, sink, stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"launch_floor_rounds": args.launch_floor, "workload": args.workload}), flush=True)
+        return
 
     if args.wg_stamps:
         def launch(i):

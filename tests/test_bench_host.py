@@ -105,3 +105,29 @@ def test_profile_commands_parse_with_this_bench():
     for md, argv in cmds:
         args = parser.parse_args(argv)
         assert args.workload in bench.WORKLOADS, (md, argv)
+
+
+def test_trace_follow_reads_kernels_by_their_predecessor(tmp_path, capsys):
+    """--trace-follow: each kernel's traced duration and the gap before it,
+    keyed by the kernel that ran before it on the same queue."""
+    import csv as _csv
+    import json as _json
+
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    rows = [  # queue, name, start, end (ns)
+        (1, "fd::split_mfma_kernel", 0, 80_000), (1, "fd::merge_kernel<128>", 80_000, 84_500),
+        (1, "fd::split_mfma_kernel", 84_500, 164_500), (1, "at::elementwise_kernel", 164_500, 169_100),
+        (1, "at::elementwise_kernel", 169_100, 173_700), (2, "fd::split_mfma_kernel", 0, 70_000),
+        (1, "fd::split_mfma_kernel", 174_700, 254_700), (1, "fd::merge_kernel<128>", 254_700, 259_500),
+    ]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        wr = _csv.writer(f)
+        wr.writerow(["Queue_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writerows(rows)
+    bench.trace_follow(str(tmp_path / "trace"))
+    out = _json.loads(capsys.readouterr().out)
+    assert out["merge_kernel after split_mfma"] == {"n": 2, "us_p10_p50_p90": [4.53, 4.65, 4.77], "gap_us_p50": 0.0}
+    assert out["elementwise after split_mfma"]["n"] == 1 and out["elementwise after elementwise"]["n"] == 1
+    assert out["split_mfma after elementwise"]["gap_us_p50"] == 1.0          # 173.7 -> 174.7 us
+    assert all("queue" not in k for k in out) and sum(v["n"] for v in out.values()) == 6
