@@ -41,6 +41,14 @@ def _case(name):
     if name == "d64_f32_valu":
         return W.contiguous(name, seed=604, batch=2, q_heads=8, kv_heads=4, head_dim=64, capacity=3000,
                             seq_lens=[3000, 999], dtype="f32"), {"force_splits": 5}
+    if name == "gqa_shifted":                  # uniform splits of two lengths (256 CUs)
+        w = W.contiguous(name, seed=605, batch=2, q_heads=64, kv_heads=8, head_dim=128, capacity=48000,
+                         seq_lens=[48000, 30001], dtype="f16")
+        return w, {"num_cus": 256, "schedule": "uniform", "host_seq_lens": w.seq_lens.tolist()}
+    if name == "paged_alternating":            # balanced ranges of alternating size (256 CUs)
+        w = W.paged(name, seed=606, batch=6, q_heads=32, kv_heads=8, head_dim=128,
+                    seq_lens=[40000, 900, 33000, 0, 29000, 30000], page_size=16, dtype="f16")
+        return w, {"num_cus": 256, "schedule": "balanced", "host_seq_lens": w.seq_lens.tolist()}
     if name == "edge_batch":
         w = W.edge_gqa_f16()
         return w, {"host_seq_lens": w.seq_lens.tolist()}
@@ -82,14 +90,18 @@ def _same_bits(a, b):
 
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["gqa_uniform", "mha_valu", "paged_balanced", "qblock_two_tiles", "d64_f32_valu",
-                                  "edge_batch"])
+                                  "edge_batch", "gqa_shifted", "paged_alternating"])
 def test_debug_barrier_build_equals_release_bitwise(name, fused):
     w, opts = _case(name)
     dev = torch.device("cuda", 0)
     prob = fd.problem_for(w.q, w.k, w.v, w.seq_lens, w.block_table, max_seq_len=w.max_seq_len)
     plan = fd.fd_plan(prob, **opts)
-    print(f"[race] {name} fused={fused} S={plan.num_splits} kernel={plan.kernel} schedule={plan.schedule}",
-          flush=True)
+    print(f"[race] {name} fused={fused} S={plan.num_splits} kernel={plan.kernel} schedule={plan.schedule} "
+          f"chunks {plan.chunk_tokens}/{plan.odd_chunk_tokens} odd_range={plan.odd_range_permille}", flush=True)
+    if name == "gqa_shifted":
+        assert plan.chunk_tokens > plan.odd_chunk_tokens
+    if name == "paged_alternating":
+        assert plan.odd_range_permille > 0
     release = _launch(fd.lib(), plan, w, dev, fused)
     debug = _launch(fd.load(DEBUG_LIB), plan, w, dev, fused)
     for what, a, b in zip(("out", "lse"), release[:2], debug[:2]):
