@@ -246,7 +246,7 @@ int split_params(const fd_plan_t* plan, const fd_args* args, float* ws_o, size_t
     p.range_odd = plan->odd_range_permille;
   } else {
     // Tokens past the last split belong to no split: clamp there as well.
-    const int64_t covered = (int64_t)(plan->num_splits / 2) * (plan->chunk_tokens + plan->odd_chunk_tokens) +
+    const int64_t covered = (int64_t)(plan->num_splits / 2) * ((int64_t)plan->chunk_tokens + plan->odd_chunk_tokens) +
                             (plan->num_splits % 2 ? plan->chunk_tokens : 0);
     if (covered < p.cap_tokens) p.cap_tokens = (int32_t)covered;
   }
