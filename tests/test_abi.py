@@ -615,6 +615,14 @@ def test_read_probe_validation_without_gpu():
     assert L.fd_read_probe(0x10000, 1 << 20, 0x20000, n - 4, None) == fd.FD_ERR_WORKSPACE
 
 
+def test_wg_stamps_only_in_the_stamp_build():
+    """The release library records no per-workgroup stamps: fd_wg_stamps
+    refuses before touching the device, whatever it is given."""
+    L = fd.lib()
+    assert L.fd_wg_stamps(0x10000, fd.WG_STAMP_RECORDS * 32, None) == fd.FD_ERR_UNSUPPORTED
+    assert L.fd_wg_stamps(None, 0, None) == fd.FD_ERR_UNSUPPORTED
+
+
 def test_problem_for_tensors():
     q = torch.zeros(2, 16, 128, dtype=torch.float16)
     k = torch.zeros(2, 4, 300, 128, dtype=torch.float16)
